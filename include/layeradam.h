@@ -1,0 +1,153 @@
+/*
+ * layeradam.h -- C ABI of the LayerAdam library (liblayeradam.so, gfx950).
+ *
+ * One call updates one decoder layer: it sums the layer's R data-parallel
+ * BF16/FP16 gradient replicas, applies one bias-corrected AdamW step to the
+ * FP32 master weights and FP32 moments (m, v) in place, and writes the BF16
+ * compute copy of the new master weights -- in one fused pass over HBM on the
+ * caller's HIP stream.
+ *
+ * Where the operation is defined:
+ *  - The state is the mixed-precision Adam state of "SlideDP: Scaling
+ *    Host-Resident LLM Fine-Tuning Across Multiple GPUs", section 前置知识
+ *    (preliminaries): BF16/FP16 weights and gradients 2N bytes each, FP32
+ *    master 4N, FP32 Adam m and v 8N -- 16N bytes in all (la_state_bytes).
+ *  - The same page, sections 核心方法 (core method) and 方法步骤详情
+ *    (method details): one authoritative FP32 master and (m, v) per layer,
+ *    updated once per iteration from one aggregated gradient (the replicas
+ *    reduced on the GPU), after which the next BF16 delivery of the layer
+ *    may go out. The page runs the update ("LayerAdam") on host CPUs; this
+ *    library runs reduction, update and cast as one GPU kernel.
+ *  - "An Efficient Heterogeneous Co-Design for Fine-Tuning on a Single GPU"
+ *    (SlideFormer), technical summary 2.2: gradients in a BF16/FP16 buffer,
+ *    FP32 -> BF16 conversion of the master for the compute copy, and
+ *    preallocated fixed-size buffers (so the library allocates nothing).
+ *  - The pages print no Adam formula. The update is PyTorch's AdamW, the
+ *    optimizer of the FSDP2 runs SlideDP checks its loss against (section
+ *    实验结果, results):
+ *        g   = (G_0 + G_1 + ... + G_{R-1}) * grad_unscale   (left to right)
+ *        m   = beta1*m + (1-beta1)*g
+ *        v   = beta2*v + (1-beta2)*(g*g)
+ *        p   = p*(1 - lr*weight_decay)
+ *              - lr/(1-beta1^t) * m / (sqrt(v)/sqrt(1-beta2^t) + eps)
+ *        w   = BF16(p), round to nearest, ties to even; NaN -> 0x7FC0
+ *    in FP32, one rounding per operation and no fused multiply-add; the
+ *    nine constants beta1, 1-beta1, beta2, 1-beta2, lr/(1-beta1^t),
+ *    sqrt(1-beta2^t), eps, 1-lr*weight_decay and grad_unscale are computed
+ *    on the host in double and rounded to FP32 once per call.
+ *
+ * Memory and ownership: every buffer is caller-owned device memory of the
+ * current HIP device. The library never allocates, never synchronises and
+ * keeps no pointer after a call returns. Calls are asynchronous on the given
+ * stream; buffers must stay alive until the stream reaches the work.
+ *
+ * Thread safety: no global mutable state apart from a thread-local error
+ * message and a per-device cache of the compute-unit count.
+ */
+#ifndef LAYERADAM_H
+#define LAYERADAM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LA_API __attribute__((visibility("default")))
+
+#define LA_MAX_REPLICAS 8   /* R in [1, 8]                                  */
+#define LA_MAX_TENSORS 256  /* tensors per call (split into several launches) */
+#define LA_ALIGNMENT 16     /* bytes; every non-empty buffer must be aligned  */
+
+typedef enum {
+  LA_OK = 0,
+  LA_ERR_INVALID_ARGUMENT = 1, /* NULL where a pointer is needed, bad count,
+                                  hyperparameter outside its domain        */
+  LA_ERR_MISALIGNED = 2,       /* a buffer not 16-byte aligned              */
+  LA_ERR_ALIASING = 3,         /* written ranges overlap each other or a
+                                  gradient                                  */
+  LA_ERR_UNSUPPORTED = 4,      /* unknown gradient dtype                    */
+  LA_ERR_HIP = 5               /* the HIP runtime refused the launch        */
+} la_status;
+
+typedef enum { LA_GRAD_BF16 = 0, LA_GRAD_FP16 = 1 } la_grad_dtype;
+
+/* One tensor of the layer. All arrays hold `numel` elements, contiguous.
+ * master, exp_avg, exp_avg_sq are read and written in place; weight_bf16 is
+ * written only (BF16 bit patterns); grads[0..R-1] are read only, in the
+ * layer's gradient dtype. Gradient replicas may alias one another (passing
+ * one buffer R times is legal); no written array may overlap any other array
+ * of the call. numel == 0 tensors are skipped and their pointers ignored. */
+typedef struct {
+  float *master;
+  float *exp_avg;
+  float *exp_avg_sq;
+  uint16_t *weight_bf16;
+  const void *grads[LA_MAX_REPLICAS];
+  int64_t numel;
+} la_tensor_desc;
+
+/* The layer: a host array of num_tensors descriptors (0 <= num_tensors <=
+ * LA_MAX_TENSORS; 0 is a no-op), the number of replicas R and their dtype
+ * (la_grad_dtype). The descriptor array is read during the call only. */
+typedef struct {
+  const la_tensor_desc *tensors;
+  int32_t num_tensors;
+  int32_t num_replicas;
+  int32_t grad_dtype;
+} la_layer_desc;
+
+/* Hyperparameters of one step. step is the 1-based count of the update being
+ * applied (t >= 1). Domains: 0 <= beta1, beta2 < 1; lr, eps, weight_decay
+ * finite and >= 0; grad_unscale finite and > 0 (1.0 = none; 1/R gives the
+ * mean of the replicas instead of their sum). */
+typedef struct {
+  double lr;
+  double beta1;
+  double beta2;
+  double eps;
+  double weight_decay;
+  int64_t step;
+  double grad_unscale;
+} la_adam_params;
+
+/* Enqueue one LayerAdam update of `layer` on `hip_stream` (a hipStream_t;
+ * NULL = the null stream).
+ *
+ * overflow_flag: NULL, or a 4-byte-aligned int32 in device memory that the
+ * kernel sets to 1 if some aggregated gradient element (after the unscale)
+ * is +-Inf or NaN. The library never clears it: the caller zeroes it, may
+ * share it across the layers of a step, and reads it after synchronising.
+ * The update is applied either way; non-finite values propagate by IEEE
+ * rules into m, v, master and the BF16 copy.
+ *
+ * Returns LA_OK once the work is enqueued. Every argument is checked on the
+ * host before anything is enqueued; on any other status nothing is enqueued
+ * and la_last_error() describes the problem. Device faults surface at the
+ * caller's next synchronisation, not here. */
+LA_API la_status layer_adam_step(const la_layer_desc *layer,
+                                 const la_adam_params *hp,
+                                 int32_t *overflow_flag, void *hip_stream);
+
+/* Bytes of mixed-precision Adam state the layer stands for: 16 per
+ * parameter (2 BF16 weight + 2 gradient + 4 FP32 master + 8 FP32 m and v).
+ * -1 if the descriptor is invalid. Host only. */
+LA_API int64_t la_state_bytes(const la_layer_desc *layer);
+
+/* Bytes one layer_adam_step moves to and from HBM in the ideal case:
+ * (2R + 26) per parameter = R gradient reads + master, m, v read and written
+ * + the BF16 write. -1 if the descriptor is invalid. Host only. */
+LA_API int64_t la_traffic_bytes(const la_layer_desc *layer);
+
+/* Message of the calling thread's last failed call ("" if none). The pointer
+ * stays valid until that thread's next call into the library. */
+LA_API const char *la_last_error(void);
+
+/* Library version and the GPU target it was built for. */
+LA_API const char *la_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LAYERADAM_H */

@@ -1,0 +1,48 @@
+// Internal interface between the C ABI layer (la_api.cpp) and the kernels
+// (la_kernel.hip). Not installed; callers use include/layeradam.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+constexpr int kMaxReplicas = 8;
+// Tensors per kernel launch: their pointers travel in the kernel arguments
+// (about 104 bytes per tensor at R = 8).
+constexpr int kTensorsPerLaunch = 16;
+
+// The FP32 constants of one step, derived on the host.
+struct Scalars {
+  float b1, c1;   // beta1, 1 - beta1
+  float b2, c2;   // beta2, 1 - beta2
+  float alpha;    // lr / (1 - beta1^t)
+  float q;        // sqrt(1 - beta2^t)
+  float e;        // eps
+  float d;        // 1 - lr * weight_decay
+  float u;        // gradient unscale factor
+};
+
+// One non-empty tensor, already validated (16-byte aligned, disjoint).
+struct TensorArgs {
+  float* p;
+  float* m;
+  float* v;
+  uint16_t* w;
+  const uint16_t* g[kMaxReplicas];
+  int64_t numel;
+};
+
+struct LaunchShape {
+  int grid_cap;   // upper bound on workgroups of one launch
+};
+
+// Enqueue the update of `count` (1..kTensorsPerLaunch) tensors in one launch.
+hipError_t launch_layer_adam(const TensorArgs* tensors, int count, int replicas,
+                             bool fp16, const Scalars& s, int32_t* flag,
+                             hipStream_t stream, const LaunchShape& shape);
+
+// Elements one workgroup processes per chunk.
+int64_t chunk_elements();
+
+}  // namespace la

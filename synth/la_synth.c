@@ -44,14 +44,14 @@ static inline double uniform01(uint64_t bits) {
   return (double)(bits >> 11) * 0x1.0p-53; /* [0, 1) */
 }
 
-/* Standard normal for element i of the stream with this key. */
-static inline double normal_at(uint64_t key, int64_t i) {
-  uint64_t k = (uint64_t)i >> 1;
+/* Standard normals of the pair k: elements 2k (cosine) and 2k+1 (sine). */
+static inline void normal_pair(uint64_t key, uint64_t k, double *z0, double *z1) {
   double u0 = uniform01(draw(key, 2 * k));
   double u1 = uniform01(draw(key, 2 * k + 1));
   double radius = sqrt(-2.0 * log(1.0 - u0));
   double angle = 6.283185307179586476925 * u1;
-  return (i & 1) ? radius * sin(angle) : radius * cos(angle);
+  *z0 = radius * cos(angle);
+  *z1 = radius * sin(angle);
 }
 
 static inline uint32_t f32_bits(float x) {
@@ -97,20 +97,31 @@ typedef struct {
   int half_format;     /* 0 BF16, 1 FP16 */
 } job;
 
+static inline void put(const job *j, int64_t i, double z) {
+  if (j->kind == KIND_NORMAL_F32) {
+    ((float *)j->out)[i] = (float)(j->a + j->b * z);
+  } else {
+    float x = (float)(j->b * j->scale * z);
+    if (j->outlier_prob > 0.0 &&
+        uniform01(draw(j->outlier_key, (uint64_t)i)) < j->outlier_prob)
+      x = x * j->outlier_mult;
+    ((uint16_t *)j->out)[i] = j->half_format ? to_fp16_rtz(x) : to_bf16_rtz(x);
+  }
+}
+
 static void run_job(const job *j) {
-  for (int64_t i = j->begin; i < j->end; ++i) {
-    if (j->kind == KIND_UNIFORM_F32) {
+  if (j->kind == KIND_UNIFORM_F32) {
+    for (int64_t i = j->begin; i < j->end; ++i) {
       double u = uniform01(draw(j->key, (uint64_t)i));
       ((float *)j->out)[i] = (float)(j->a + (j->b - j->a) * u);
-    } else if (j->kind == KIND_NORMAL_F32) {
-      ((float *)j->out)[i] = (float)(j->a + j->b * normal_at(j->key, i));
-    } else {
-      float x = (float)(j->b * j->scale * normal_at(j->key, i));
-      if (j->outlier_prob > 0.0 &&
-          uniform01(draw(j->outlier_key, (uint64_t)i)) < j->outlier_prob)
-        x = x * j->outlier_mult;
-      ((uint16_t *)j->out)[i] = j->half_format ? to_fp16_rtz(x) : to_bf16_rtz(x);
     }
+    return;
+  }
+  for (int64_t k = j->begin >> 1; 2 * k < j->end; ++k) {
+    double z0, z1;
+    normal_pair(j->key, (uint64_t)k, &z0, &z1);
+    if (2 * k >= j->begin) put(j, 2 * k, z0);
+    if (2 * k + 1 < j->end) put(j, 2 * k + 1, z1);
   }
 }
 

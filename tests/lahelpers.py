@@ -1,0 +1,179 @@
+"""Shared pieces of the GPU tests: upload seeded inputs, run the HIP path
+through the C ABI, run the oracle on the same inputs, compare.
+
+Comparison rule: master, m and v within 2 FP32 ulp (ordered-integer distance,
++0 and -0 equal, NaN only against NaN); the BF16 copy bit-exact, both against
+the oracle's RNE cast of the GPU's own master and against the oracle's BF16.
+"""
+from __future__ import annotations
+
+import sys
+from dataclasses import dataclass
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+import torch
+
+import optimizer_step_layeradam_amd as la
+import oracle
+import synth
+
+ULP_TOL = 2
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def ordered(x: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(x, np.float32).view(np.int32).astype(np.int64)
+    return np.where(b < 0, -(b & 0x7FFFFFFF), b)
+
+
+def ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    a = np.asarray(a, np.float32)
+    b = np.asarray(b, np.float32)
+    d = np.abs(ordered(a) - ordered(b))
+    na, nb = np.isnan(a), np.isnan(b)
+    d = np.where(na & nb, 0, d)
+    d = np.where(na ^ nb, np.iinfo(np.int64).max, d)
+    return d
+
+
+def grad_torch_dtype(w: synth.Workload):
+    return torch.float16 if w.grad_dtype == "fp16" else torch.bfloat16
+
+
+def to_device_u16(a: np.ndarray, dtype, device) -> torch.Tensor:
+    return torch.from_numpy(a.view(np.int16)).to(device).view(dtype)
+
+
+class GpuLayer:
+    """One workload's inputs resident on the GPU, laid out as the benchmark
+    lays them out: one allocation per master/m/v/BF16 tensor, one flat
+    buffer per gradient replica with tensor views at multiples of 8."""
+
+    def __init__(self, L: synth.LayerInputs, device="cuda:0"):
+        self.L = L
+        w = L.workload
+        dev = torch.device(device)
+        gdt = grad_torch_dtype(w)
+        self.params = []
+        for i, (_, n) in enumerate(w.tensors):
+            p = torch.from_numpy(L.master[i]).to(dev)
+            m = torch.from_numpy(L.exp_avg[i]).to(dev)
+            v = torch.from_numpy(L.exp_avg_sq[i]).to(dev)
+            wb = torch.full((n,), 0x7FAA, dtype=torch.int16, device=dev).view(torch.bfloat16)
+            self.params.append((p, m, v, wb))
+        self.grad_flat = [to_device_u16(g, gdt, dev) for g in L.grad_flat]
+        self.grads = [[gf[off:off + n] for gf in self.grad_flat]
+                      for off, (_, n) in zip(L.grad_offsets, w.tensors)]
+        self.flag = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def step(self, t: Optional[int] = None, with_flag: Optional[bool] = None, **hp_over):
+        w = self.L.workload
+        hp = dict(w.hyper)
+        hp.update(hp_over)
+        unscale = hp.pop("unscale", w.unscale)
+        use_flag = w.with_flag if with_flag is None else with_flag
+        la.step(self.params, self.grads, step=w.step if t is None else t,
+                grad_unscale=unscale, overflow_flag=self.flag if use_flag else None, **hp)
+
+    def download(self) -> Dict[str, List[np.ndarray]]:
+        torch.cuda.synchronize()
+        out = {"master": [], "exp_avg": [], "exp_avg_sq": [], "weight_bf16": []}
+        for p, m, v, wb in self.params:
+            out["master"].append(p.cpu().numpy())
+            out["exp_avg"].append(m.cpu().numpy())
+            out["exp_avg_sq"].append(v.cpu().numpy())
+            out["weight_bf16"].append(wb.view(torch.int16).cpu().numpy().view(np.uint16))
+        out["flag"] = int(self.flag.item())
+        return out
+
+    def free(self):
+        self.params = self.grads = self.grad_flat = None
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def oracle_tensors(L: synth.LayerInputs, idx: Optional[Sequence[np.ndarray]] = None):
+    w = L.workload
+    ts = []
+    for i, (_, n) in enumerate(w.tensors):
+        sel = slice(None) if idx is None else idx[i]
+        g = [np.ascontiguousarray(L.grad(r, i)[sel]) for r in range(w.replicas)]
+        p = np.array(L.master[i][sel], np.float32)
+        ts.append(oracle.Tensor(p, np.array(L.exp_avg[i][sel], np.float32),
+                                np.array(L.exp_avg_sq[i][sel], np.float32),
+                                np.zeros(p.size, np.uint16), g))
+    return ts
+
+
+def oracle_step(L: synth.LayerInputs, ts, t: Optional[int] = None,
+                with_flag: Optional[bool] = None, **hp_over) -> Optional[int]:
+    w = L.workload
+    hp = dict(w.hyper)
+    hp.update(hp_over)
+    unscale = hp.pop("unscale", w.unscale)
+    use_flag = w.with_flag if with_flag is None else with_flag
+    return oracle.step(ts, dtype=w.grad_dtype, step=w.step if t is None else t,
+                       unscale=unscale, with_flag=use_flag, **hp)
+
+
+@dataclass
+class Report:
+    compared: int = 0
+    max_ulp: int = 0
+    nonzero_ulp: int = 0
+    bf16_mismatch: int = 0
+
+    def __str__(self):
+        return (f"compared={self.compared} max_ulp={self.max_ulp} "
+                f"nonzero_ulp={self.nonzero_ulp} bf16_mismatch={self.bf16_mismatch}")
+
+
+def compare(gpu: Dict[str, List[np.ndarray]], ts, idx=None, report: Optional[Report] = None,
+            label: str = "") -> Report:
+    """Compare GPU outputs (whole tensors, or sampled at idx) with oracle
+    tensors; assert the parity bar and return statistics."""
+    rep = report or Report()
+    for i, x in enumerate(ts):
+        sel = slice(None) if idx is None else idx[i]
+        for field in ("master", "exp_avg", "exp_avg_sq"):
+            g = gpu[field][i][sel]
+            o = getattr(x, field)
+            d = ulp_distance(g, o)
+            worst = int(d.max()) if d.size else 0
+            if worst > ULP_TOL:
+                j = int(np.argmax(d))
+                raise AssertionError(f"{label} tensor {i} {field}[{j}]: gpu={g[j]!r} "
+                                     f"oracle={o[j]!r} ({worst} ulp)")
+            rep.max_ulp = max(rep.max_ulp, worst)
+            rep.nonzero_ulp += int(np.count_nonzero(d))
+        gw = gpu["weight_bf16"][i][sel]
+        # the BF16 copy is exactly the RNE cast of the GPU's own master ...
+        own = oracle.round_bf16(gpu["master"][i][sel])
+        bad = np.nonzero(gw != own)[0]
+        if bad.size:
+            j = int(bad[0])
+            raise AssertionError(f"{label} tensor {i} weight_bf16[{j}] = {gw[j]:#06x}, "
+                                 f"RNE(master) = {own[j]:#06x}")
+        # ... and equals the oracle's wherever the masters agree bit for bit
+        same = gpu["master"][i][sel].view(np.uint32) == x.master.view(np.uint32)
+        rep.bf16_mismatch += int(np.count_nonzero((gw != x.weight_bf16) & same))
+        assert rep.bf16_mismatch == 0, f"{label} tensor {i}: BF16 differs where masters agree"
+        rep.compared += int(gw.size)
+    return rep
+
+
+def sample_indices(w: synth.Workload, per_tensor: int, seed: int = 0) -> List[np.ndarray]:
+    """Sorted unique indices per tensor: the first and last 4096 elements, the
+    whole final chunk region, and `per_tensor` uniform draws."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _, n in w.tensors:
+        parts = [np.arange(min(n, 4096)), np.arange(max(0, n - 8192), n),
+                 rng.integers(0, n, min(n, per_tensor))]
+        out.append(np.unique(np.concatenate(parts)).astype(np.int64))
+    return out

@@ -1,0 +1,216 @@
+"""The C-ABI library on the host: it loads, exports what include/layeradam.h
+declares, accounts bytes as the pages do, and rejects bad arguments before
+anything reaches a GPU. No kernel runs here.
+
+The argument-validation cases use made-up device addresses; every one of them
+is invalid on purpose and must be refused on the host. They are skipped
+where a GPU is visible, so that no such address can ever reach a device.
+"""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  (load torch's HIP runtime before the library)
+
+import optimizer_step_layeradam_amd as la
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "layeradam.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "state_accounting.json")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"LA_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(la.EXPORTS)
+    lib = ctypes.CDLL(la.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_names_the_target():
+    assert "gfx950" in la.version()
+
+
+def test_header_compiles_as_c():
+    import subprocess
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "t.c")
+        with open(src, "w") as f:
+            f.write('#include "layeradam.h"\nint main(void){ la_layer_desc d = {0};'
+                    ' return (int)la_state_bytes(&d); }\n')
+        subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-c", "-I",
+                        os.path.join(ROOT, "include"), src, "-o", os.path.join(d, "t.o")],
+                       check=True)
+
+
+# ---------------------------------------------------------------------------
+# Byte accounting against the pages' printed values
+# ---------------------------------------------------------------------------
+def test_state_bytes_match_the_pages():
+    g = json.load(open(GOLDEN))
+    per = g["bytes_per_param"]
+    assert (per["bf16_or_fp16_weights"] + per["bf16_or_fp16_gradients"] + per["fp32_master"]
+            + per["fp32_adam_m_and_v"]) == per["total"] == 16
+    assert la.state_bytes([1]) == per["total"]
+    # master + m + v share of the state: 12 bytes per parameter
+    assert per["fp32_master"] + per["fp32_adam_m_and_v"] == g["master_plus_moments_bytes_per_param"]["value"]
+    for inst in g["instances"]:
+        n = inst["params"]
+        # split the count over several tensors, as a real layer list would be
+        numels = [n // 4] * 3 + [n - 3 * (n // 4)]
+        b = la.state_bytes(numels)
+        if "state_bytes_greater_than" in inst:
+            assert b > inst["state_bytes_greater_than"]
+        if "state_bytes_at_least" in inst:
+            assert b >= inst["state_bytes_at_least"]
+        assert b == 16 * n
+
+
+@pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
+def test_traffic_bytes_of_each_workload(name):
+    w = synth.WORKLOADS[name]
+    numels = [n for _, n in w.tensors]
+    assert la.traffic_bytes(numels, w.replicas) == (2 * w.replicas + 26) * w.numel
+    assert la.traffic_bytes(numels, w.replicas) == w.traffic_bytes
+
+
+def test_workload_sizes():
+    # parameter counts of the layer shapes (tensor list: q, k, v, o, gate, up,
+    # down and two norms)
+    expect = {"tiny": 274_432, "qwen3_4b_layer": 100_930_560,
+              "qwen3_14b_layer": 330_311_680, "flat_800m": 800_000_003,
+              "qwen25_72b_layer": 877_674_496}
+    for name, n in expect.items():
+        assert synth.WORKLOADS[name].numel == n
+
+
+def test_accounting_rejects_bad_descriptors():
+    desc, keep = la.make_layer([dict(numel=10)], 0, la.GRAD_BF16)
+    assert la.state_bytes_raw(desc) == -1
+    desc, keep = la.make_layer([dict(numel=-1)], 1, la.GRAD_BF16)
+    assert la.traffic_bytes_raw(desc) == -1
+
+
+# ---------------------------------------------------------------------------
+# Validation, all on the host
+# ---------------------------------------------------------------------------
+host_only = pytest.mark.skipif(torch.cuda.is_available(),
+                               reason="uses made-up device addresses; host-only check")
+
+BASE = 0x7F0000000000  # made-up, 16-byte aligned; never dereferenced
+HP = dict(lr=1e-5, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=1)
+
+
+def fake_tensor(k, n=1024, R=2):
+    base = BASE + k * 0x100000000
+    return dict(master=base, exp_avg=base + 0x10000000, exp_avg_sq=base + 0x20000000,
+                weight_bf16=base + 0x30000000,
+                grads=[base + 0x40000000 + r * 0x1000000 for r in range(R)], numel=n)
+
+
+def expect_status(tensors, R, dtype, hp, status, flag=0):
+    desc, keep = la.make_layer(tensors, R, dtype)
+    with pytest.raises(la.LayerAdamError) as e:
+        la.step_raw(desc, la.make_params(**hp), flag)
+    assert e.value.status == status, str(e.value)
+    assert la.last_error() != ""
+
+
+@host_only
+@pytest.mark.parametrize("R", [0, 9, -1])
+def test_replica_count_out_of_range(R):
+    expect_status([fake_tensor(0)], R, la.GRAD_BF16, HP, 1)
+
+
+@host_only
+def test_unknown_gradient_dtype():
+    expect_status([fake_tensor(0)], 2, 7, HP, 4)
+
+
+@host_only
+@pytest.mark.parametrize("bad", [dict(step=0), dict(step=-5), dict(beta1=1.0), dict(beta1=-0.1),
+                                 dict(beta2=1.0), dict(lr=-1e-3), dict(lr=float("inf")),
+                                 dict(eps=float("nan")), dict(weight_decay=-0.1),
+                                 dict(grad_unscale=0.0), dict(grad_unscale=float("inf")),
+                                 dict(grad_unscale=-1.0)])
+def test_hyperparameters_outside_their_domain(bad):
+    hp = dict(HP, grad_unscale=1.0)
+    hp.update(bad)
+    expect_status([fake_tensor(0)], 2, la.GRAD_BF16, hp, 1)
+
+
+@host_only
+@pytest.mark.parametrize("field", ["master", "exp_avg", "exp_avg_sq", "weight_bf16", "grad1"])
+def test_null_buffer(field):
+    t = fake_tensor(0)
+    if field == "grad1":
+        t["grads"][1] = 0
+    else:
+        t[field] = 0
+    expect_status([t], 2, la.GRAD_BF16, HP, 1)
+
+
+@host_only
+@pytest.mark.parametrize("field", ["master", "exp_avg", "exp_avg_sq", "weight_bf16", "grad0"])
+def test_misaligned_buffer(field):
+    t = fake_tensor(0)
+    if field == "grad0":
+        t["grads"][0] += 8
+    else:
+        t[field] += 4
+    expect_status([t], 2, la.GRAD_BF16, HP, 2)
+
+
+@host_only
+def test_misaligned_flag():
+    expect_status([fake_tensor(0)], 2, la.GRAD_BF16, HP, 2, flag=BASE + 0x50000002)
+
+
+@host_only
+@pytest.mark.parametrize("case", ["m_on_master", "w_inside_v", "across_tensors", "grad_on_w",
+                                  "flag_in_master"])
+def test_overlapping_buffers(case):
+    a, b = fake_tensor(0), fake_tensor(1)
+    flag = 0
+    if case == "m_on_master":
+        a["exp_avg"] = a["master"] + 16
+    elif case == "w_inside_v":
+        a["weight_bf16"] = a["exp_avg_sq"] + 2048
+    elif case == "across_tensors":
+        b["master"] = a["exp_avg"] + 1024
+    elif case == "grad_on_w":
+        b["grads"][1] = a["weight_bf16"]
+    elif case == "flag_in_master":
+        flag = a["master"] + 64
+    expect_status([a, b], 2, la.GRAD_BF16, HP, 3, flag=flag)
+
+
+@host_only
+def test_too_many_tensors():
+    expect_status([fake_tensor(k % 4, n=0) for k in range(la.MAX_TENSORS + 1)], 2,
+                  la.GRAD_BF16, HP, 1)
+
+
+@host_only
+def test_negative_numel():
+    t = fake_tensor(0)
+    t["numel"] = -3
+    expect_status([t], 2, la.GRAD_BF16, HP, 1)
+
+
+def test_no_tensors_or_only_empty_tensors_enqueue_nothing():
+    # nothing to launch: succeeds without touching the device
+    desc, keep = la.make_layer([], 3, la.GRAD_BF16)
+    la.step_raw(desc, la.make_params(**HP))
+    desc, keep = la.make_layer([dict(numel=0), dict(numel=0)], 3, la.GRAD_FP16)
+    la.step_raw(desc, la.make_params(**HP))
+    assert la.last_error() == ""
