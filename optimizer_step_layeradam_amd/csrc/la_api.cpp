@@ -52,16 +52,20 @@ int compute_units(int device) {
   return n;
 }
 
-// Workgroups per compute unit for the persistent grid. LAYERADAM_BLOCKS_PER_CU
-// overrides the default (read once).
+// Upper bound on the grid of one launch. Default: one workgroup per chunk up
+// to 2^30 workgroups (the kernel strides past that). LAYERADAM_BLOCKS_PER_CU
+// (1..64, read once) caps the grid at that many workgroups per compute unit
+// instead, making the kernel persistent; kept for launch-shape comparisons.
 int blocks_per_cu() {
   static const int value = [] {
     const char* env = std::getenv("LAYERADAM_BLOCKS_PER_CU");
     int v = env ? std::atoi(env) : 0;
-    return (v >= 1 && v <= 64) ? v : 8;
+    return (v >= 1 && v <= 64) ? v : 0;
   }();
   return value;
 }
+
+constexpr int kMaxGrid = 1 << 30;
 
 bool finite_nonneg(double x) { return std::isfinite(x) && x >= 0.0; }
 
@@ -231,10 +235,15 @@ LA_API la_status layer_adam_step(const la_layer_desc* layer, const la_adam_param
       hipError_t e = hipGetDevice(&device);
       if (e != hipSuccess)
         return fail(LA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
-      const int cus = compute_units(device);
-      if (cus <= 0) return fail(LA_ERR_HIP, "cannot read the compute-unit count of device %d",
-                                device);
-      shape.grid_cap = cus * blocks_per_cu();
+      const int per_cu = blocks_per_cu();
+      if (per_cu == 0) {
+        shape.grid_cap = kMaxGrid;
+      } else {
+        const int cus = compute_units(device);
+        if (cus <= 0)
+          return fail(LA_ERR_HIP, "cannot read the compute-unit count of device %d", device);
+        shape.grid_cap = cus * per_cu;
+      }
     }
     hipError_t e = la::launch_layer_adam(batch, pending, layer->num_replicas,
                                          layer->grad_dtype == LA_GRAD_FP16, s, overflow_flag,

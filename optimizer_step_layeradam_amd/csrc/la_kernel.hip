@@ -11,14 +11,17 @@
 // conversion the SlideFormer page (technical summary 2.2) does on the host.
 //
 // Work decomposition. Every tensor of a launch is cut into chunks of
-// kChunk elements (the last chunk of a tensor may be partial). Workgroups
-// walk the global chunk list with a grid stride, so one launch covers all
-// tensors of the layer and the grid can be sized to the chip, not to the
-// layer. A chunk is U tiles of 256 threads x 4 elements: each thread owns
-// 4 consecutive elements per tile, so one wave's loads are contiguous
-// 1 KiB (FP32, 16 B per lane) and 512 B (16-bit gradients, 8 B per lane)
-// runs. A thread issues every load of its U tiles before any arithmetic,
-// which keeps (12 + 2R) * 4 * U bytes per lane in flight.
+// kChunk elements (the last chunk of a tensor may be partial); one launch
+// covers all tensors of the layer. By default there is one workgroup per
+// chunk: the dispatcher then keeps the workgroups in flight on a narrow,
+// advancing window of every stream, which measured faster on MI355X than a
+// persistent grid whose workgroups drift apart (the loop below still
+// strides by the grid when the grid is capped). A chunk is U tiles of 256
+// threads x 4 elements: each thread owns 4 consecutive elements per tile,
+// so one wave's accesses are contiguous 1 KiB (FP32, 16 B per lane) and
+// 512 B (16-bit gradients, 8 B per lane) runs. A thread issues every load
+// of its U tiles before any arithmetic, (12 + 2R) * 4 * U bytes per lane in
+// flight. Every access carries the non-temporal hint: nothing is reused.
 //
 // Arithmetic is IEEE binary32 with one rounding per operation: contraction
 // into fused multiply-adds is switched off for this file, and division and
@@ -34,10 +37,54 @@
 namespace la {
 namespace {
 
-constexpr int kBlock = 256;          // threads per workgroup (4 waves)
-constexpr int kVec = 4;              // consecutive elements per thread per tile
-constexpr int kUnroll = 2;           // tiles per chunk
+// Tile shape and cache hints. The defaults are the measured best on MI355X
+// for the Qwen3-14B-shaped layer at R = 8; the macros exist so that other
+// shapes can be built and compared.
+#ifndef LA_BLOCK
+#define LA_BLOCK 256
+#endif
+#ifndef LA_TILE_VEC
+#define LA_TILE_VEC 4
+#endif
+#ifndef LA_TILE_UNROLL
+#define LA_TILE_UNROLL 4
+#endif
+#ifndef LA_NT_LOADS
+#define LA_NT_LOADS 1
+#endif
+#ifndef LA_NT_STORES
+#define LA_NT_STORES 1
+#endif
+#ifndef LA_WAVE_CONTIG
+#define LA_WAVE_CONTIG 1   // 1: each wave's tiles are adjacent in memory
+#endif
+#ifndef LA_STREAM_MAJOR
+#define LA_STREAM_MAJOR 0  // 1: issue all tiles of one stream before the next stream
+#endif
+
+constexpr int kBlock = LA_BLOCK;        // threads per workgroup
+constexpr int kVec = LA_TILE_VEC;       // consecutive elements per thread per tile (4 or 8)
+constexpr int kUnroll = LA_TILE_UNROLL; // tiles per chunk
 constexpr int kChunk = kBlock * kVec * kUnroll;
+constexpr int kQuads = kVec / 4;        // 16-byte FP32 vectors per array per tile
+static_assert(kVec == 4 || kVec == 8, "4 or 8 elements per thread per tile");
+static_assert(kBlock % 64 == 0 && kBlock <= 1024, "whole waves");
+
+// Native vector types (the non-temporal builtins need them).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t grad_words __attribute__((ext_vector_type(kVec / 2)));  // kVec 16-bit values
+
+template <typename T>
+__device__ __forceinline__ T load_stream(const T* p) {
+  if constexpr (LA_NT_LOADS) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <typename T>
+__device__ __forceinline__ void store_stream(T v, T* p) {
+  if constexpr (LA_NT_STORES) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
 
 template <int R>
 struct KernelTensor {
@@ -111,6 +158,17 @@ __device__ __forceinline__ Elem adam_update(float g, float p, float m, float v,
   return {p_new, m_new, v_new};
 }
 
+// Element offset, within its chunk, of thread tid's first element in tile u.
+// Tile-major: tile u covers [u * kBlock * kVec, (u + 1) * kBlock * kVec).
+// Wave-contiguous: wave w owns kUnroll adjacent runs of 64 * kVec elements.
+__device__ __forceinline__ uint32_t tile_offset(int u, int tid) {
+  if constexpr (LA_WAVE_CONTIG) {
+    return static_cast<uint32_t>((((tid >> 6) * kUnroll + u) * 64 + (tid & 63)) * kVec);
+  } else {
+    return static_cast<uint32_t>((u * kBlock + tid) * kVec);
+  }
+}
+
 // ---- the kernel ---------------------------------------------------------------
 template <int R, bool FP16, bool FLAG>
 __global__ void __launch_bounds__(kBlock)
@@ -141,50 +199,70 @@ layer_adam_kernel(const KernelArgs<R> a) {
 
     if (base + kChunk <= n) {
       // Full chunk: vector loads of every tile first, then the arithmetic.
-      float4 P[kUnroll], M[kUnroll], V[kUnroll];
-      uint2 G[kUnroll][R];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const uint32_t off = static_cast<uint32_t>((u * kBlock + tid) * kVec);
-        P[u] = *reinterpret_cast<const float4*>(p + off);
-        M[u] = *reinterpret_cast<const float4*>(m + off);
-        V[u] = *reinterpret_cast<const float4*>(v + off);
+      f32x4 P[kUnroll][kQuads], M[kUnroll][kQuads], V[kUnroll][kQuads];
+      grad_words G[kUnroll][R];
+      if constexpr (LA_STREAM_MAJOR) {
 #pragma unroll
         for (int r = 0; r < R; ++r)
-          G[u][r] = *reinterpret_cast<const uint2*>(g[r] + off);
+#pragma unroll
+          for (int u = 0; u < kUnroll; ++u)
+            G[u][r] = load_stream(reinterpret_cast<const grad_words*>(g[r] + tile_offset(u, tid)));
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+          for (int q = 0; q < kQuads; ++q)
+            P[u][q] = load_stream(reinterpret_cast<const f32x4*>(p + tile_offset(u, tid)) + q);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+          for (int q = 0; q < kQuads; ++q)
+            M[u][q] = load_stream(reinterpret_cast<const f32x4*>(m + tile_offset(u, tid)) + q);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+          for (int q = 0; q < kQuads; ++q)
+            V[u][q] = load_stream(reinterpret_cast<const f32x4*>(v + tile_offset(u, tid)) + q);
+      } else {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const uint32_t off = tile_offset(u, tid);
+#pragma unroll
+          for (int q = 0; q < kQuads; ++q) {
+            P[u][q] = load_stream(reinterpret_cast<const f32x4*>(p + off) + q);
+            M[u][q] = load_stream(reinterpret_cast<const f32x4*>(m + off) + q);
+            V[u][q] = load_stream(reinterpret_cast<const f32x4*>(v + off) + q);
+          }
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+            G[u][r] = load_stream(reinterpret_cast<const grad_words*>(g[r] + off));
+        }
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const uint32_t off = static_cast<uint32_t>((u * kBlock + tid) * kVec);
-        float gs[kVec];
-        gs[0] = decode_lo<FP16>(G[u][0].x);
-        gs[1] = decode_hi<FP16>(G[u][0].x);
-        gs[2] = decode_lo<FP16>(G[u][0].y);
-        gs[3] = decode_hi<FP16>(G[u][0].y);
-#pragma unroll
-        for (int r = 1; r < R; ++r) {
-          gs[0] = gs[0] + decode_lo<FP16>(G[u][r].x);
-          gs[1] = gs[1] + decode_hi<FP16>(G[u][r].x);
-          gs[2] = gs[2] + decode_lo<FP16>(G[u][r].y);
-          gs[3] = gs[3] + decode_hi<FP16>(G[u][r].y);
-        }
-        const float pv[kVec] = {P[u].x, P[u].y, P[u].z, P[u].w};
-        const float mv[kVec] = {M[u].x, M[u].y, M[u].z, M[u].w};
-        const float vv[kVec] = {V[u].x, V[u].y, V[u].z, V[u].w};
+        const uint32_t off = tile_offset(u, tid);
         Elem e[kVec];
 #pragma unroll
         for (int k = 0; k < kVec; ++k) {
-          const float gk = gs[k] * s.u;
+          // left fold over the replicas, in replica order
+          float gk = (k & 1) ? decode_hi<FP16>(G[u][0][k / 2]) : decode_lo<FP16>(G[u][0][k / 2]);
+#pragma unroll
+          for (int r = 1; r < R; ++r)
+            gk = gk + ((k & 1) ? decode_hi<FP16>(G[u][r][k / 2]) : decode_lo<FP16>(G[u][r][k / 2]));
+          gk = gk * s.u;
           if (FLAG) bad |= !__builtin_isfinite(gk);
-          e[k] = adam_update(gk, pv[k], mv[k], vv[k], s);
+          e[k] = adam_update(gk, P[u][k / 4][k % 4], M[u][k / 4][k % 4], V[u][k / 4][k % 4], s);
         }
-        *reinterpret_cast<float4*>(p + off) = make_float4(e[0].p, e[1].p, e[2].p, e[3].p);
-        *reinterpret_cast<float4*>(m + off) = make_float4(e[0].m, e[1].m, e[2].m, e[3].m);
-        *reinterpret_cast<float4*>(v + off) = make_float4(e[0].v, e[1].v, e[2].v, e[3].v);
-        uint2 wb;
-        wb.x = bf16_bits(e[0].p) | (bf16_bits(e[1].p) << 16);
-        wb.y = bf16_bits(e[2].p) | (bf16_bits(e[3].p) << 16);
-        *reinterpret_cast<uint2*>(w + off) = wb;
+#pragma unroll
+        for (int q = 0; q < kQuads; ++q) {
+          const Elem* x = e + 4 * q;
+          store_stream(f32x4{x[0].p, x[1].p, x[2].p, x[3].p}, reinterpret_cast<f32x4*>(p + off) + q);
+          store_stream(f32x4{x[0].m, x[1].m, x[2].m, x[3].m}, reinterpret_cast<f32x4*>(m + off) + q);
+          store_stream(f32x4{x[0].v, x[1].v, x[2].v, x[3].v}, reinterpret_cast<f32x4*>(v + off) + q);
+        }
+        grad_words wb;
+#pragma unroll
+        for (int k = 0; k < kVec; k += 2) wb[k / 2] = bf16_bits(e[k].p) | (bf16_bits(e[k + 1].p) << 16);
+        store_stream(wb, reinterpret_cast<grad_words*>(w + off));
       }
     } else {
       // Last, partial chunk of a tensor: element by element, bounds-checked.
@@ -235,7 +313,7 @@ hipError_t launch_typed(const TensorArgs* ts, int count, const Scalars& s,
   a.s = s;
   a.flag = flag;
   a.count = count;
-  const int64_t grid = chunks < shape.grid_cap ? chunks : shape.grid_cap;
+  const int64_t grid = chunks < shape.grid_cap ? chunks : shape.grid_cap;  // >= 1
   void* args[] = {&a};
   return hipLaunchKernel(reinterpret_cast<const void*>(&layer_adam_kernel<R, FP16, FLAG>),
                          dim3(static_cast<unsigned>(grid)), dim3(kBlock), args, 0, stream);
