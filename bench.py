@@ -155,6 +155,29 @@ def _cpu_model():
     return None
 
 
+def copy_reference(torch, mib: int = 2048, reps: int = 10):
+    """Bandwidth of a plain device-to-device copy on this GPU (context for
+    the roofline: what streaming one read and one write stream achieves)."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    gbs = 2 * n * 4 * reps / (a.elapsed_time(b) / 1e3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"gbs": gbs, "frac_of_peak": gbs / PEAK_HBM_GBS, "bytes_per_copy": 2 * n * 4,
+            "kernel": "Tensor.copy_ (device copy)"}
+
+
 def calibrate_copy(mib: int, reps: int):
     """A plain device-to-device copy of known size, for scaling the HBM byte
     counters (run under rocprofv3 --pmc)."""
@@ -282,6 +305,7 @@ def main():
                      "median_launch_ms": statistics.median(launch_ms),
                      "min_launch_ms": min(launch_ms), "max_launch_ms": max(launch_ms)},
         "overflow_flag_first_step": flag_first,
+        "hbm_copy_reference": copy_reference(torch),
         "cpu_baseline": None,
     }
     if first is not None:
