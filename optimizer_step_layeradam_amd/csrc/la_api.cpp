@@ -36,35 +36,46 @@ la_status ok() {
   return LA_OK;
 }
 
-// Compute units of each device, read once (hipDeviceGetAttribute is cheap,
-// but this keeps the per-call host path to a few hundred nanoseconds).
+// Per-device launch facts, read once per device: the LDS of one compute
+// unit and the most one workgroup may take. (hipDeviceGetAttribute is cheap;
+// caching keeps the per-call host path to a few hundred nanoseconds.)
 constexpr int kMaxDevices = 64;
-std::atomic<int> g_cu_count[kMaxDevices];
+std::atomic<int> g_lds_reserve[kMaxDevices];  // bytes + 1; 0 = not read yet
 
-int compute_units(int device) {
-  if (device < 0 || device >= kMaxDevices) return 0;
-  int n = g_cu_count[device].load(std::memory_order_relaxed);
-  if (n > 0) return n;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
-      n <= 0)
-    return 0;
-  g_cu_count[device].store(n, std::memory_order_relaxed);
-  return n;
+// LDS to reserve per workgroup so that at most `per_cu` workgroups fit on a
+// compute unit: floor(lds_per_cu / (per_cu + 1/2)), within the per-workgroup
+// limit. 0 (no reservation) when no cap is wanted or the facts are missing.
+int lds_reserve(int device, int per_cu) {
+  if (per_cu <= 0 || device < 0 || device >= kMaxDevices) return 0;
+  const int cached = g_lds_reserve[device].load(std::memory_order_relaxed);
+  if (cached > 0) return cached - 1;
+  int per_cu_bytes = 0, per_block_bytes = 0;
+  int bytes = 0;
+  if (hipDeviceGetAttribute(&per_cu_bytes, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                            device) == hipSuccess &&
+      hipDeviceGetAttribute(&per_block_bytes, hipDeviceAttributeMaxSharedMemoryPerBlock,
+                            device) == hipSuccess &&
+      per_cu_bytes > 0 && per_block_bytes > 0) {
+    bytes = static_cast<int>(2LL * per_cu_bytes / (2LL * per_cu + 1)) / 1024 * 1024;
+    if (bytes > per_block_bytes) bytes = 0;  // cannot cap this way on this device
+  }
+  g_lds_reserve[device].store(bytes + 1, std::memory_order_relaxed);
+  return bytes;
 }
 
-// Upper bound on the grid of one launch. Default: one workgroup per chunk up
-// to 2^30 workgroups (the kernel strides past that). LAYERADAM_BLOCKS_PER_CU
-// (1..64, read once) caps the grid at that many workgroups per compute unit
-// instead, making the kernel persistent; kept for launch-shape comparisons.
-int blocks_per_cu() {
+// Workgroups resident per compute unit. LAYERADAM_WORKGROUPS_PER_CU (0..64,
+// read once) overrides the built-in target; 0 removes the cap.
+int workgroups_per_cu() {
   static const int value = [] {
-    const char* env = std::getenv("LAYERADAM_BLOCKS_PER_CU");
-    int v = env ? std::atoi(env) : 0;
-    return (v >= 1 && v <= 64) ? v : 0;
+    const char* env = std::getenv("LAYERADAM_WORKGROUPS_PER_CU");
+    if (env == nullptr) return la::target_workgroups_per_cu();
+    const int v = std::atoi(env);
+    return (v >= 0 && v <= 64) ? v : la::target_workgroups_per_cu();
   }();
   return value;
 }
 
+// One workgroup per chunk up to this many; the kernel strides past it.
 constexpr int kMaxGrid = 1 << 30;
 
 bool finite_nonneg(double x) { return std::isfinite(x) && x >= 0.0; }
@@ -226,7 +237,7 @@ LA_API la_status layer_adam_step(const la_layer_desc* layer, const la_adam_param
   int pending = 0;
   int launches = 0;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  la::LaunchShape shape{0};
+  la::LaunchShape shape{0, 0};
 
   auto flush = [&]() -> la_status {
     if (pending == 0) return LA_OK;
@@ -235,15 +246,8 @@ LA_API la_status layer_adam_step(const la_layer_desc* layer, const la_adam_param
       hipError_t e = hipGetDevice(&device);
       if (e != hipSuccess)
         return fail(LA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
-      const int per_cu = blocks_per_cu();
-      if (per_cu == 0) {
-        shape.grid_cap = kMaxGrid;
-      } else {
-        const int cus = compute_units(device);
-        if (cus <= 0)
-          return fail(LA_ERR_HIP, "cannot read the compute-unit count of device %d", device);
-        shape.grid_cap = cus * per_cu;
-      }
+      shape.grid_cap = kMaxGrid;
+      shape.lds_bytes = lds_reserve(device, workgroups_per_cu());
     }
     hipError_t e = la::launch_layer_adam(batch, pending, layer->num_replicas,
                                          layer->grad_dtype == LA_GRAD_FP16, s, overflow_flag,

@@ -35,7 +35,12 @@ struct TensorArgs {
 
 struct LaunchShape {
   int grid_cap;   // upper bound on workgroups of one launch
+  int lds_bytes;  // LDS reserved per workgroup (unused by the kernel); caps
+                  // how many workgroups a compute unit holds at once
 };
+
+// Workgroups resident per compute unit that the launch aims for.
+int target_workgroups_per_cu();
 
 // Enqueue the update of `count` (1..kTensorsPerLaunch) tensors in one launch.
 hipError_t launch_layer_adam(const TensorArgs* tensors, int count, int replicas,

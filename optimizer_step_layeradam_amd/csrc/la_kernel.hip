@@ -12,15 +12,19 @@
 //
 // Work decomposition. Every tensor of a launch is cut into chunks of
 // kChunk elements (the last chunk of a tensor may be partial); one launch
-// covers all tensors of the layer. By default there is one workgroup per
-// chunk: the dispatcher then keeps the workgroups in flight on a narrow,
-// advancing window of every stream, which measured faster on MI355X than a
+// covers all tensors of the layer. There is one workgroup per chunk: the
+// dispatcher then keeps the workgroups in flight on a narrow, advancing
+// window of every stream, which measured faster on MI355X than a
 // persistent grid whose workgroups drift apart (the loop below still
-// strides by the grid when the grid is capped). A chunk is U tiles of 256
-// threads x 4 elements: each thread owns 4 consecutive elements per tile,
-// so one wave's accesses are contiguous 1 KiB (FP32, 16 B per lane) and
-// 512 B (16-bit gradients, 8 B per lane) runs. A thread issues every load
-// of its U tiles before any arithmetic, (12 + 2R) * 4 * U bytes per lane in
+// strides by the grid when the grid is capped). The launch also reserves
+// LDS that the kernel never touches, so that a compute unit holds only two
+// workgroups (four waves, one per SIMD) at a time: fewer requests in flight
+// interleave the 2R + 8 streams less at the HBM, and that measured fastest.
+// A chunk is U tiles of 128 threads x 4 elements: each thread owns 4
+// consecutive elements per tile and a wave's U tiles are adjacent, so a wave
+// reads U KiB runs of each FP32 stream (16 B per lane) and U/2 KiB runs of
+// each 16-bit gradient stream (8 B per lane). A thread issues every load of
+// its U tiles before any arithmetic, (12 + 2R) * 4 * U bytes per lane in
 // flight. Every access carries the non-temporal hint: nothing is reused.
 //
 // Arithmetic is IEEE binary32 with one rounding per operation: contraction
@@ -41,7 +45,7 @@ namespace {
 // for the Qwen3-14B-shaped layer at R = 8; the macros exist so that other
 // shapes can be built and compared.
 #ifndef LA_BLOCK
-#define LA_BLOCK 256
+#define LA_BLOCK 128
 #endif
 #ifndef LA_TILE_VEC
 #define LA_TILE_VEC 4
@@ -60,6 +64,12 @@ namespace {
 #endif
 #ifndef LA_STREAM_MAJOR
 #define LA_STREAM_MAJOR 0  // 1: issue all tiles of one stream before the next stream
+#endif
+#ifndef LA_STORE_MAJOR
+#define LA_STORE_MAJOR 0   // 1: compute every tile, then store stream by stream
+#endif
+#ifndef LA_WORKGROUPS_PER_CU
+#define LA_WORKGROUPS_PER_CU 2  // resident workgroups per compute unit (0: no cap)
 #endif
 
 constexpr int kBlock = LA_BLOCK;        // threads per workgroup
@@ -169,6 +179,22 @@ __device__ __forceinline__ uint32_t tile_offset(int u, int tid) {
   }
 }
 
+// Store one tile's results: master, m, v as 16-byte vectors, BF16 packed.
+__device__ __forceinline__ void store_tile(const Elem* e, float* p, float* m, float* v,
+                                           uint16_t* w, uint32_t off) {
+#pragma unroll
+  for (int q = 0; q < kQuads; ++q) {
+    const Elem* x = e + 4 * q;
+    store_stream(f32x4{x[0].p, x[1].p, x[2].p, x[3].p}, reinterpret_cast<f32x4*>(p + off) + q);
+    store_stream(f32x4{x[0].m, x[1].m, x[2].m, x[3].m}, reinterpret_cast<f32x4*>(m + off) + q);
+    store_stream(f32x4{x[0].v, x[1].v, x[2].v, x[3].v}, reinterpret_cast<f32x4*>(v + off) + q);
+  }
+  grad_words wb;
+#pragma unroll
+  for (int k = 0; k < kVec; k += 2) wb[k / 2] = bf16_bits(e[k].p) | (bf16_bits(e[k + 1].p) << 16);
+  store_stream(wb, reinterpret_cast<grad_words*>(w + off));
+}
+
 // ---- the kernel ---------------------------------------------------------------
 template <int R, bool FP16, bool FLAG>
 __global__ void __launch_bounds__(kBlock)
@@ -237,10 +263,9 @@ layer_adam_kernel(const KernelArgs<R> a) {
             G[u][r] = load_stream(reinterpret_cast<const grad_words*>(g[r] + off));
         }
       }
+      Elem e[kUnroll][kVec];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const uint32_t off = tile_offset(u, tid);
-        Elem e[kVec];
 #pragma unroll
         for (int k = 0; k < kVec; ++k) {
           // left fold over the replicas, in replica order
@@ -250,19 +275,43 @@ layer_adam_kernel(const KernelArgs<R> a) {
             gk = gk + ((k & 1) ? decode_hi<FP16>(G[u][r][k / 2]) : decode_lo<FP16>(G[u][r][k / 2]));
           gk = gk * s.u;
           if (FLAG) bad |= !__builtin_isfinite(gk);
-          e[k] = adam_update(gk, P[u][k / 4][k % 4], M[u][k / 4][k % 4], V[u][k / 4][k % 4], s);
+          e[u][k] = adam_update(gk, P[u][k / 4][k % 4], M[u][k / 4][k % 4], V[u][k / 4][k % 4], s);
         }
+        if constexpr (!LA_STORE_MAJOR) store_tile(e[u], p, m, v, w, tile_offset(u, tid));
+      }
+      if constexpr (LA_STORE_MAJOR) {
 #pragma unroll
-        for (int q = 0; q < kQuads; ++q) {
-          const Elem* x = e + 4 * q;
-          store_stream(f32x4{x[0].p, x[1].p, x[2].p, x[3].p}, reinterpret_cast<f32x4*>(p + off) + q);
-          store_stream(f32x4{x[0].m, x[1].m, x[2].m, x[3].m}, reinterpret_cast<f32x4*>(m + off) + q);
-          store_stream(f32x4{x[0].v, x[1].v, x[2].v, x[3].v}, reinterpret_cast<f32x4*>(v + off) + q);
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+          for (int q = 0; q < kQuads; ++q) {
+            const Elem* x = e[u] + 4 * q;
+            store_stream(f32x4{x[0].p, x[1].p, x[2].p, x[3].p},
+                         reinterpret_cast<f32x4*>(p + tile_offset(u, tid)) + q);
+          }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+          for (int q = 0; q < kQuads; ++q) {
+            const Elem* x = e[u] + 4 * q;
+            store_stream(f32x4{x[0].m, x[1].m, x[2].m, x[3].m},
+                         reinterpret_cast<f32x4*>(m + tile_offset(u, tid)) + q);
+          }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+          for (int q = 0; q < kQuads; ++q) {
+            const Elem* x = e[u] + 4 * q;
+            store_stream(f32x4{x[0].v, x[1].v, x[2].v, x[3].v},
+                         reinterpret_cast<f32x4*>(v + tile_offset(u, tid)) + q);
+          }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          grad_words wb;
+#pragma unroll
+          for (int k = 0; k < kVec; k += 2)
+            wb[k / 2] = bf16_bits(e[u][k].p) | (bf16_bits(e[u][k + 1].p) << 16);
+          store_stream(wb, reinterpret_cast<grad_words*>(w + tile_offset(u, tid)));
         }
-        grad_words wb;
-#pragma unroll
-        for (int k = 0; k < kVec; k += 2) wb[k / 2] = bf16_bits(e[k].p) | (bf16_bits(e[k + 1].p) << 16);
-        store_stream(wb, reinterpret_cast<grad_words*>(w + off));
       }
     } else {
       // Last, partial chunk of a tensor: element by element, bounds-checked.
@@ -316,7 +365,7 @@ hipError_t launch_typed(const TensorArgs* ts, int count, const Scalars& s,
   const int64_t grid = chunks < shape.grid_cap ? chunks : shape.grid_cap;  // >= 1
   void* args[] = {&a};
   return hipLaunchKernel(reinterpret_cast<const void*>(&layer_adam_kernel<R, FP16, FLAG>),
-                         dim3(static_cast<unsigned>(grid)), dim3(kBlock), args, 0, stream);
+                         dim3(static_cast<unsigned>(grid)), dim3(kBlock), args, static_cast<unsigned>(shape.lds_bytes), stream);
 }
 
 template <int R>
@@ -333,6 +382,8 @@ hipError_t launch_r(const TensorArgs* ts, int count, bool fp16, const Scalars& s
 }  // namespace
 
 int64_t chunk_elements() { return kChunk; }
+
+int target_workgroups_per_cu() { return LA_WORKGROUPS_PER_CU; }
 
 hipError_t launch_layer_adam(const TensorArgs* tensors, int count, int replicas,
                              bool fp16, const Scalars& s, int32_t* flag,
