@@ -123,7 +123,7 @@ def cpu_baseline(L, first, budget_s: float):
                     d = np.abs(g - o)
                     worst_ulp = max(worst_ulp, int(d.max()))
                     nonzero += int(np.count_nonzero(d))
-                bf16_bad += int(np.count_nonzero(first["weight_bf16"][i][a:b] != t.weight_bf16))
+                bf16_bad += int(np.count_nonzero(first["weight_out"][i][a:b] != t.weight_out))
                 done[i] = b
     finally:
         if old_aff is not None:
@@ -239,12 +239,12 @@ def main():
     torch.cuda.synchronize()
     first = None
     if not args.no_cpu_baseline:
-        first = {"master": [], "exp_avg": [], "exp_avg_sq": [], "weight_bf16": []}
+        first = {"master": [], "exp_avg": [], "exp_avg_sq": [], "weight_out": []}
         for p, m, v, wb in params:
             first["master"].append(p.cpu().numpy())
             first["exp_avg"].append(m.cpu().numpy())
             first["exp_avg_sq"].append(v.cpu().numpy())
-            first["weight_bf16"].append(wb.view(torch.int16).cpu().numpy().view(np.uint16))
+            first["weight_out"].append(wb.view(torch.int16).cpu().numpy().view(np.uint16))
     flag_first = int(flag.item()) if flag is not None else None
 
     t = w.step + 1

@@ -26,6 +26,7 @@ _LIB_OVERRIDE = os.environ.get("LA_ORACLE_LIB_OVERRIDE")
 
 MAX_REPLICAS = 8
 GRAD_DTYPES = {"bf16": 0, "fp16": 1}
+OUT_DTYPES = {"bf16": 0, "fp16": 1, "none": 2}
 
 # The flags matter for the result: no contraction of a*b+c into a fused
 # multiply-add, no fast-math, default x86-64 SSE arithmetic (no x87).
@@ -48,7 +49,7 @@ class _Tensor(ctypes.Structure):
         ("master", ctypes.c_void_p),
         ("exp_avg", ctypes.c_void_p),
         ("exp_avg_sq", ctypes.c_void_p),
-        ("weight_bf16", ctypes.c_void_p),
+        ("weight_out", ctypes.c_void_p),
         ("grad", ctypes.c_void_p * MAX_REPLICAS),
         ("numel", ctypes.c_int64),
     ]
@@ -80,9 +81,14 @@ def _load():
     lib.lao_round_bf16.argtypes = [ctypes.c_float]
     lib.lao_round_bf16.restype = ctypes.c_uint16
     lib.lao_step.argtypes = [ctypes.POINTER(_Tensor), ctypes.c_int, ctypes.c_int,
-                             ctypes.c_int] + [ctypes.c_double] * 5 + [
+                             ctypes.c_int, ctypes.c_int] + [ctypes.c_double] * 5 + [
         ctypes.c_int64, ctypes.c_double, ctypes.POINTER(ctypes.c_int32)]
     lib.lao_step.restype = ctypes.c_int
+    lib.lao_check_finite.argtypes = [ctypes.POINTER(_Tensor), ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, ctypes.c_double]
+    lib.lao_check_finite.restype = ctypes.c_int
+    lib.lao_round_fp16_array.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
+    lib.lao_round_fp16_array.restype = None
     lib.lao_decode_array.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_int64, ctypes.c_int]
     lib.lao_decode_array.restype = None
@@ -131,6 +137,13 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     return out
 
 
+def round_fp16(x: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint16)
+    _load().lao_round_fp16_array(_ptr(x), _ptr(out), x.size)
+    return out
+
+
 def aggregate(grads: Sequence[np.ndarray], dtype: str, unscale: float = 1.0) -> np.ndarray:
     grads = [np.ascontiguousarray(g, dtype=np.uint16) for g in grads]
     n = grads[0].size
@@ -146,12 +159,13 @@ def aggregate(grads: Sequence[np.ndarray], dtype: str, unscale: float = 1.0) -> 
 
 @dataclass
 class Tensor:
-    """One tensor of a layer: FP32 master/m/v (updated in place), the BF16
-    output (written) and the R gradient replicas (uint16 bit patterns)."""
+    """One tensor of a layer: FP32 master/m/v (updated in place), the
+    compute-copy output (BF16 or FP16 bit patterns, written) and the R
+    gradient replicas (uint16 bit patterns)."""
     master: np.ndarray
     exp_avg: np.ndarray
     exp_avg_sq: np.ndarray
-    weight_bf16: np.ndarray
+    weight_out: np.ndarray
     grads: List[np.ndarray] = field(default_factory=list)
 
     @property
@@ -159,13 +173,7 @@ class Tensor:
         return self.master.size
 
 
-def step(tensors: Sequence[Tensor], *, dtype: str, lr: float, beta1: float,
-         beta2: float, eps: float, weight_decay: float, step: int,
-         unscale: float = 1.0, with_flag: bool = False) -> Optional[int]:
-    """Run one oracle update over ``tensors`` in place. Returns the overflow
-    flag (0/1) when ``with_flag`` is set, else None."""
-    if not tensors:
-        raise ValueError("oracle.step: no tensors")
+def _table(tensors: Sequence[Tensor], need_out: bool):
     replicas = len(tensors[0].grads)
     arr = (_Tensor * len(tensors))()
     for i, t in enumerate(tensors):
@@ -173,21 +181,44 @@ def step(tensors: Sequence[Tensor], *, dtype: str, lr: float, beta1: float,
         _check(t.master, np.float32, n, "master")
         _check(t.exp_avg, np.float32, n, "exp_avg")
         _check(t.exp_avg_sq, np.float32, n, "exp_avg_sq")
-        _check(t.weight_bf16, np.uint16, n, "weight_bf16")
+        if need_out:
+            _check(t.weight_out, np.uint16, n, "weight_out")
+            arr[i].weight_out = _ptr(t.weight_out)
         if len(t.grads) != replicas:
-            raise ValueError("oracle.step: every tensor needs the same R")
+            raise ValueError("oracle: every tensor needs the same R")
         arr[i].master = _ptr(t.master)
         arr[i].exp_avg = _ptr(t.exp_avg)
         arr[i].exp_avg_sq = _ptr(t.exp_avg_sq)
-        arr[i].weight_bf16 = _ptr(t.weight_bf16)
         for r, g in enumerate(t.grads):
             _check(g, np.uint16, n, f"grad[{r}]")
             arr[i].grad[r] = _ptr(g)
         arr[i].numel = n
+    return arr, replicas
+
+
+def step(tensors: Sequence[Tensor], *, dtype: str, lr: float, beta1: float,
+         beta2: float, eps: float, weight_decay: float, step: int,
+         unscale: float = 1.0, with_flag: bool = False,
+         out_dtype: str = "bf16") -> Optional[int]:
+    """Run one oracle update over ``tensors`` in place. The compute copy goes
+    to each tensor's ``weight_out`` array in ``out_dtype`` ("bf16", "fp16"
+    or "none"). Returns the overflow flag (0/1) when ``with_flag`` is set."""
+    if not tensors:
+        raise ValueError("oracle.step: no tensors")
+    arr, replicas = _table(tensors, out_dtype != "none")
     flag = ctypes.c_int32(0)
-    rc = _load().lao_step(arr, len(tensors), replicas, GRAD_DTYPES[dtype], lr,
-                          beta1, beta2, eps, weight_decay, step, unscale,
-                          ctypes.byref(flag) if with_flag else None)
+    rc = _load().lao_step(arr, len(tensors), replicas, GRAD_DTYPES[dtype],
+                          OUT_DTYPES[out_dtype], lr, beta1, beta2, eps, weight_decay,
+                          step, unscale, ctypes.byref(flag) if with_flag else None)
     if rc != 0:
         raise ValueError("oracle.step: invalid arguments")
     return int(flag.value) if with_flag else None
+
+
+def check_finite(tensors: Sequence[Tensor], *, dtype: str, unscale: float = 1.0) -> int:
+    """1 if some aggregated gradient element is +-Inf or NaN, else 0."""
+    arr, replicas = _table(tensors, False)
+    rc = _load().lao_check_finite(arr, len(tensors), replicas, GRAD_DTYPES[dtype], unscale)
+    if rc < 0:
+        raise ValueError("oracle.check_finite: invalid arguments")
+    return rc

@@ -97,6 +97,38 @@ uint16_t lao_round_bf16(float x) {
 }
 
 /* ------------------------------------------------------------------------ */
+/* FP32 -> FP16 (IEEE binary16), round to nearest, ties to even.             */
+/* Written from the format: a normal binary16 is (1024 + f) * 2^(e - 25)     */
+/* for biased exponent e in 1..30, a subnormal is f * 2^-24. Scale |x| so    */
+/* that the binary16 significand becomes the integer part, round that       */
+/* integer to nearest-even in double (exact: x has 24 significant bits),     */
+/* and let a carry to 2048 move to the next binade (and from the top binade  */
+/* to Inf).                                                                  */
+/* ------------------------------------------------------------------------ */
+uint16_t lao_round_fp16(float x) {
+  if (isnan(x)) return 0x7E00;
+  uint16_t sign = signbit(x) ? 0x8000 : 0x0000;
+  double a = fabs((double)x);
+  if (isinf(x)) return sign | 0x7C00;
+  if (a < ldexp(1.0, -14)) {
+    /* subnormal range: units of 2^-24; 1024 units is the smallest normal */
+    double units = nearbyint(ldexp(a, 24));
+    return sign | (uint16_t)units;
+  }
+  int e2;
+  frexp(a, &e2);                 /* a = m * 2^e2 with m in [0.5, 1) */
+  int unbiased = e2 - 1;         /* a in [2^unbiased, 2^(unbiased+1)) */
+  double significand = nearbyint(ldexp(a, 10 - unbiased)); /* in [1024, 2048] */
+  if (significand == 2048.0) {
+    significand = 1024.0;
+    unbiased += 1;
+  }
+  int biased = unbiased + 15;
+  if (biased >= 31) return sign | 0x7C00;
+  return sign | (uint16_t)(biased << 10) | (uint16_t)(significand - 1024.0);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Aggregated gradient of one element: the sum of the R data-parallel        */
 /* replicas (SlideDP: one aggregated gradient per layer per iteration,       */
 /* reduced on the GPU before the update), left to right, then the unscale    */
@@ -118,7 +150,7 @@ float lao_aggregate(const uint16_t *const *grad, int replicas, int dtype,
 /* ------------------------------------------------------------------------ */
 static void update_element(const lao_scalars *s, float g, float *master,
                            float *exp_avg, float *exp_avg_sq,
-                           uint16_t *weight_bf16) {
+                           uint16_t *weight_out, int out_dtype) {
   float m = *exp_avg;
   float v = *exp_avg_sq;
   float p = *master;
@@ -148,11 +180,12 @@ static void update_element(const lao_scalars *s, float g, float *master,
   *exp_avg = m;
   *exp_avg_sq = v;
   *master = p;
-  *weight_bf16 = lao_round_bf16(p);
+  if (out_dtype == LAO_OUT_BF16) *weight_out = lao_round_bf16(p);
+  if (out_dtype == LAO_OUT_FP16) *weight_out = lao_round_fp16(p);
 }
 
 int lao_step(lao_tensor *tensors, int num_tensors, int replicas, int dtype,
-             double lr, double beta1, double beta2, double eps,
+             int out_dtype, double lr, double beta1, double beta2, double eps,
              double weight_decay, int64_t step, double unscale,
              int32_t *flag) {
   lao_scalars s;
@@ -160,15 +193,17 @@ int lao_step(lao_tensor *tensors, int num_tensors, int replicas, int dtype,
   if (num_tensors < 0) return -1;
   if (replicas < 1 || replicas > LAO_MAX_REPLICAS) return -1;
   if (dtype != LAO_GRAD_BF16 && dtype != LAO_GRAD_FP16) return -1;
+  if (out_dtype != LAO_OUT_BF16 && out_dtype != LAO_OUT_FP16 && out_dtype != LAO_OUT_NONE)
+    return -1;
   if (lao_derive_scalars(lr, beta1, beta2, eps, weight_decay, step, unscale,
                          &s) != 0)
     return -1;
   for (int t = 0; t < num_tensors; ++t) {
     if (tensors[t].numel < 0) return -1;
     if (tensors[t].numel == 0) continue;
-    if (!tensors[t].master || !tensors[t].exp_avg || !tensors[t].exp_avg_sq ||
-        !tensors[t].weight_bf16)
+    if (!tensors[t].master || !tensors[t].exp_avg || !tensors[t].exp_avg_sq)
       return -1;
+    if (out_dtype != LAO_OUT_NONE && !tensors[t].weight_out) return -1;
     for (int r = 0; r < replicas; ++r)
       if (!tensors[t].grad[r]) return -1;
   }
@@ -178,11 +213,32 @@ int lao_step(lao_tensor *tensors, int num_tensors, int replicas, int dtype,
     for (int64_t j = 0; j < x->numel; ++j) {
       float g = lao_aggregate(x->grad, replicas, dtype, j, s.u);
       if (flag != NULL && !isfinite(g)) *flag = 1;
-      update_element(&s, g, &x->master[j], &x->exp_avg[j],
-                     &x->exp_avg_sq[j], &x->weight_bf16[j]);
+      update_element(&s, g, &x->master[j], &x->exp_avg[j], &x->exp_avg_sq[j],
+                     out_dtype == LAO_OUT_NONE ? NULL : &x->weight_out[j],
+                     out_dtype);
     }
   }
   return 0;
+}
+
+int lao_check_finite(const lao_tensor *tensors, int num_tensors, int replicas,
+                     int dtype, double unscale) {
+  if (tensors == NULL && num_tensors != 0) return -1;
+  if (num_tensors < 0 || replicas < 1 || replicas > LAO_MAX_REPLICAS) return -1;
+  if (dtype != LAO_GRAD_BF16 && dtype != LAO_GRAD_FP16) return -1;
+  if (!(unscale > 0.0) || !isfinite(unscale)) return -1;
+  float u = (float)unscale;
+  int found = 0;
+  for (int t = 0; t < num_tensors; ++t) {
+    if (tensors[t].numel < 0) return -1;
+    for (int r = 0; r < replicas && tensors[t].numel > 0; ++r)
+      if (!tensors[t].grad[r]) return -1;
+    for (int64_t j = 0; j < tensors[t].numel; ++j) {
+      float g = lao_aggregate(tensors[t].grad, replicas, dtype, j, u);
+      if (!isfinite(g)) found = 1;
+    }
+  }
+  return found;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -194,6 +250,10 @@ void lao_decode_array(const uint16_t *in, float *out, int64_t n, int dtype) {
 
 void lao_round_bf16_array(const float *in, uint16_t *out, int64_t n) {
   for (int64_t i = 0; i < n; ++i) out[i] = lao_round_bf16(in[i]);
+}
+
+void lao_round_fp16_array(const float *in, uint16_t *out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = lao_round_fp16(in[i]);
 }
 
 void lao_aggregate_array(const uint16_t *const *grad, int replicas, int dtype,

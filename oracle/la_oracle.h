@@ -13,7 +13,7 @@
  *   v   = b2*v + c2*(g*g)
  *   den = sqrt(v)/q + e
  *   p   = p*d - alpha*(m/den)
- *   w   = round-to-nearest-even BF16 of p
+ *   w   = round-to-nearest-even BF16 (or FP16) of p, or nothing
  * with b1, c1, b2, c2, alpha, q, e, d, u derived once per call in double and
  * rounded to FP32 (see lao_derive_scalars).
  *
@@ -54,12 +54,17 @@ extern "C" {
 #define LAO_GRAD_BF16 0
 #define LAO_GRAD_FP16 1
 
+/* compute-copy formats */
+#define LAO_OUT_BF16 0
+#define LAO_OUT_FP16 1
+#define LAO_OUT_NONE 2
+
 /* One tensor of a layer, as host arrays of numel elements each. */
 typedef struct {
   float *master;                          /* FP32, updated in place        */
   float *exp_avg;                         /* m, FP32, updated in place     */
   float *exp_avg_sq;                      /* v, FP32, updated in place     */
-  uint16_t *weight_bf16;                  /* BF16 bit patterns, written    */
+  uint16_t *weight_out;                   /* BF16/FP16 bits, written       */
   const uint16_t *grad[LAO_MAX_REPLICAS]; /* R replicas, BF16/FP16 bits    */
   int64_t numel;
 } lao_tensor;
@@ -91,23 +96,36 @@ float lao_decode(uint16_t bits, int dtype);
  * finite BF16 by half an ulp or more become +-Inf; every NaN becomes 0x7FC0. */
 uint16_t lao_round_bf16(float x);
 
+/* FP16 (IEEE binary16) nearest to x, ties to the even significand, with
+ * binary16 subnormals; magnitudes at or past 65520 (half an ulp above the
+ * largest finite 65504) become +-Inf; every NaN becomes 0x7E00. */
+uint16_t lao_round_fp16(float x);
+
 /* Aggregated gradient of element j: left fold over replicas 0..R-1 in FP32,
  * then one multiply by u. */
 float lao_aggregate(const uint16_t *const *grad, int replicas, int dtype,
                     int64_t j, float u);
 
-/* One LayerAdam update of every element of every tensor. If flag is not NULL
- * it is set to 1 when some aggregated gradient is +-Inf or NaN (never cleared;
- * the update is still applied). Returns 0, or -1 on invalid arguments (then
- * nothing is written). */
+/* One LayerAdam update of every element of every tensor. out_dtype selects
+ * the compute copy written to weight_out (LAO_OUT_NONE: none). If flag is not
+ * NULL it is set to 1 when some aggregated gradient is +-Inf or NaN (never
+ * cleared; the update is still applied). Returns 0, or -1 on invalid
+ * arguments (then nothing is written). */
 int lao_step(lao_tensor *tensors, int num_tensors, int replicas, int dtype,
-             double lr, double beta1, double beta2, double eps,
+             int out_dtype, double lr, double beta1, double beta2, double eps,
              double weight_decay, int64_t step, double unscale,
              int32_t *flag);
+
+/* 1 if some aggregated gradient element (sum of the replicas times u, as in
+ * lao_aggregate) of any tensor is +-Inf or NaN, else 0; -1 on invalid
+ * arguments. Reads the gradients only. */
+int lao_check_finite(const lao_tensor *tensors, int num_tensors, int replicas,
+                     int dtype, double unscale);
 
 /* Element-wise array forms of the helpers above, for tests. */
 void lao_decode_array(const uint16_t *in, float *out, int64_t n, int dtype);
 void lao_round_bf16_array(const float *in, uint16_t *out, int64_t n);
+void lao_round_fp16_array(const float *in, uint16_t *out, int64_t n);
 void lao_aggregate_array(const uint16_t *const *grad, int replicas, int dtype,
                          float u, float *out, int64_t n);
 

@@ -82,12 +82,12 @@ class GpuLayer:
 
     def download(self) -> Dict[str, List[np.ndarray]]:
         torch.cuda.synchronize()
-        out = {"master": [], "exp_avg": [], "exp_avg_sq": [], "weight_bf16": []}
+        out = {"master": [], "exp_avg": [], "exp_avg_sq": [], "weight_out": []}
         for p, m, v, wb in self.params:
             out["master"].append(p.cpu().numpy())
             out["exp_avg"].append(m.cpu().numpy())
             out["exp_avg_sq"].append(v.cpu().numpy())
-            out["weight_bf16"].append(wb.view(torch.int16).cpu().numpy().view(np.uint16))
+            out["weight_out"].append(wb.view(torch.int16).cpu().numpy().view(np.uint16))
         out["flag"] = int(self.flag.item())
         return out
 
@@ -151,17 +151,17 @@ def compare(gpu: Dict[str, List[np.ndarray]], ts, idx=None, report: Optional[Rep
                                      f"oracle={o[j]!r} ({worst} ulp)")
             rep.max_ulp = max(rep.max_ulp, worst)
             rep.nonzero_ulp += int(np.count_nonzero(d))
-        gw = gpu["weight_bf16"][i][sel]
+        gw = gpu["weight_out"][i][sel]
         # the BF16 copy is exactly the RNE cast of the GPU's own master ...
         own = oracle.round_bf16(gpu["master"][i][sel])
         bad = np.nonzero(gw != own)[0]
         if bad.size:
             j = int(bad[0])
-            raise AssertionError(f"{label} tensor {i} weight_bf16[{j}] = {gw[j]:#06x}, "
+            raise AssertionError(f"{label} tensor {i} weight_out[{j}] = {gw[j]:#06x}, "
                                  f"RNE(master) = {own[j]:#06x}")
         # ... and equals the oracle's wherever the masters agree bit for bit
         same = gpu["master"][i][sel].view(np.uint32) == x.master.view(np.uint32)
-        rep.bf16_mismatch += int(np.count_nonzero((gw != x.weight_bf16) & same))
+        rep.bf16_mismatch += int(np.count_nonzero((gw != x.weight_out) & same))
         assert rep.bf16_mismatch == 0, f"{label} tensor {i}: BF16 differs where masters agree"
         rep.compared += int(gw.size)
     return rep

@@ -113,7 +113,7 @@ HP = dict(lr=1e-5, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=1)
 def fake_tensor(k, n=1024, R=2):
     base = BASE + k * 0x100000000
     return dict(master=base, exp_avg=base + 0x10000000, exp_avg_sq=base + 0x20000000,
-                weight_bf16=base + 0x30000000,
+                weight_out=base + 0x30000000,
                 grads=[base + 0x40000000 + r * 0x1000000 for r in range(R)], numel=n)
 
 
@@ -149,7 +149,7 @@ def test_hyperparameters_outside_their_domain(bad):
 
 
 @host_only
-@pytest.mark.parametrize("field", ["master", "exp_avg", "exp_avg_sq", "weight_bf16", "grad1"])
+@pytest.mark.parametrize("field", ["master", "exp_avg", "exp_avg_sq", "weight_out", "grad1"])
 def test_null_buffer(field):
     t = fake_tensor(0)
     if field == "grad1":
@@ -160,7 +160,7 @@ def test_null_buffer(field):
 
 
 @host_only
-@pytest.mark.parametrize("field", ["master", "exp_avg", "exp_avg_sq", "weight_bf16", "grad0"])
+@pytest.mark.parametrize("field", ["master", "exp_avg", "exp_avg_sq", "weight_out", "grad0"])
 def test_misaligned_buffer(field):
     t = fake_tensor(0)
     if field == "grad0":
@@ -184,11 +184,11 @@ def test_overlapping_buffers(case):
     if case == "m_on_master":
         a["exp_avg"] = a["master"] + 16
     elif case == "w_inside_v":
-        a["weight_bf16"] = a["exp_avg_sq"] + 2048
+        a["weight_out"] = a["exp_avg_sq"] + 2048
     elif case == "across_tensors":
         b["master"] = a["exp_avg"] + 1024
     elif case == "grad_on_w":
-        b["grads"][1] = a["weight_bf16"]
+        b["grads"][1] = a["weight_out"]
     elif case == "flag_in_master":
         flag = a["master"] + 64
     expect_status([a, b], 2, la.GRAD_BF16, HP, 3, flag=flag)

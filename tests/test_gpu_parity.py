@@ -127,7 +127,7 @@ def test_injected_non_finite_gradients(code):
     got, _, _ = run_case(w, mutate)
     assert got["flag"] == 1
     for i, j in hits:
-        assert np.isnan(got["master"][i][j]) and got["weight_bf16"][i][j] == 0x7FC0
+        assert np.isnan(got["master"][i][j]) and got["weight_out"][i][j] == 0x7FC0
 
 
 def test_flag_stays_zero_and_is_never_cleared():
@@ -199,7 +199,7 @@ def test_every_bf16_element_is_written():
     w = synth.Workload(name="coverage", seed=2800, tensors=RAGGED, replicas=1,
                        grad_dtype="bf16", step=1)
     got, _, _ = run_case(w)
-    for wb in got["weight_bf16"]:
+    for wb in got["weight_out"]:
         assert not np.any(wb == 0x7FAA)
 
 
@@ -281,13 +281,13 @@ def test_workload_full_size(name):
         idx = sample_indices(w, per_tensor=400_000, seed=5)
         log(f"  oracle on {sum(i.size for i in idx)} sampled elements")
         torch.cuda.synchronize()
-        got = {"master": [], "exp_avg": [], "exp_avg_sq": [], "weight_bf16": []}
+        got = {"master": [], "exp_avg": [], "exp_avg_sq": [], "weight_out": []}
         for (p, m, v, wb), ii in zip(gl.params, idx):
             it = torch.from_numpy(ii).to(p.device)
             got["master"].append(p[it].cpu().numpy())
             got["exp_avg"].append(m[it].cpu().numpy())
             got["exp_avg_sq"].append(v[it].cpu().numpy())
-            got["weight_bf16"].append(wb.view(torch.int16)[it].cpu().numpy().view(np.uint16))
+            got["weight_out"].append(wb.view(torch.int16)[it].cpu().numpy().view(np.uint16))
         got["flag"] = int(gl.flag.item())
         gl.free()
         ts = oracle_tensors(L, idx)

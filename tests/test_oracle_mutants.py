@@ -53,6 +53,14 @@ MUTANTS = {
     "fp16 exponent bias off by one": ("exponent - 25", "exponent - 24"),
     "fp16 subnormal scale wrong": ("ldexpf((float)fraction, -24)", "ldexpf((float)fraction, -25)"),
     "flag never raised": ("if (flag != NULL && !isfinite(g)) *flag = 1;", ""),
+    "fp16 cast truncates": ("double significand = nearbyint(ldexp(a, 10 - unbiased));",
+                            "double significand = floor(ldexp(a, 10 - unbiased));"),
+    "fp16 cast overflows one binade late": ("if (biased >= 31) return sign | 0x7C00;",
+                                            "if (biased > 31) return sign | 0x7C00;"),
+    "fp16 subnormals flushed": ("double units = nearbyint(ldexp(a, 24));", "double units = 0.0;"),
+    "gradient check ignores the unscale": ("  float u = (float)unscale;\n  int found = 0;",
+                                           "  float u = 1.0f;\n  int found = 0;"),
+    "gradient check misses NaN": ("if (!isfinite(g)) found = 1;", "if (isinf(g)) found = 1;"),
     "L2 decay instead of decoupled": (
         "float g = lao_aggregate(x->grad, replicas, dtype, j, s.u);",
         "float g = lao_aggregate(x->grad, replicas, dtype, j, s.u) + (float)weight_decay * x->master[j];"),

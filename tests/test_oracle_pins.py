@@ -148,6 +148,34 @@ def test_round_bf16_special_values():
     assert oracle.round_bf16(f32_from_bits(np.array([0x3F818000], np.uint32)))[0] == 0x3F82
 
 
+def test_round_fp16_against_numpy():
+    """numpy's float32 -> float16 is IEEE round-to-nearest-even with
+    subnormals and overflow to Inf."""
+    rng = np.random.default_rng(17)
+    pats = np.concatenate([_structured_f32_patterns(),
+                           rng.integers(0, 2 ** 32, 4_000_000, dtype=np.uint64).astype(np.uint32)])
+    x = f32_from_bits(pats)
+    got = oracle.round_fp16(x)
+    nan = np.isnan(x)
+    assert np.all(got[nan] == 0x7E00)
+    with np.errstate(over="ignore"):
+        lib = x[~nan].astype(np.float16).view(np.uint16)
+    bad = np.nonzero(got[~nan] != lib)[0]
+    assert bad.size == 0, f"first mismatch at pattern {hex(int(pats[~nan][bad[0]]))}"
+
+
+def test_round_fp16_special_values():
+    cases = [(1.0, 0x3C00), (-2.0, 0xC000), (65504.0, 0x7BFF), (65519.99, 0x7BFF),
+             (65520.0, 0x7C00), (-65520.0, 0xFC00), (2.0 ** -24, 0x0001),
+             (2.0 ** -25, 0x0000),            # tie between 0 and 2^-24: even
+             (3 * 2.0 ** -25, 0x0002),        # tie between 1 and 2 units: even
+             (2.0 ** -14, 0x0400), (float("inf"), 0x7C00), (-0.0, 0x8000),
+             (1.0 + 2.0 ** -11, 0x3C00),      # tie: even significand
+             (1.0 + 3 * 2.0 ** -11, 0x3C02)]  # tie: even significand
+    for x, want in cases:
+        assert oracle.round_fp16(np.array([x], np.float32))[0] == want, x
+
+
 # --------------------------------------------------------------------------
 # Aggregation of the R replicas
 # --------------------------------------------------------------------------
@@ -214,7 +242,7 @@ def test_power_of_two_unscale_is_invisible(dtype):
     b = make_tensor(p, m, v, list(G_scaled))
     oracle.step([a], dtype=dtype, step=7, unscale=1.0, **HP)
     oracle.step([b], dtype=dtype, step=7, unscale=2.0 ** -10, **HP)
-    for f in ("master", "exp_avg", "exp_avg_sq", "weight_bf16"):
+    for f in ("master", "exp_avg", "exp_avg_sq", "weight_out"):
         assert np.array_equal(getattr(a, f).view(np.uint8), getattr(b, f).view(np.uint8)), f
 
 
@@ -247,7 +275,7 @@ def test_zero_learning_rate_keeps_master_and_still_moves_moments():
     x = make_tensor(p, m, v, [g])
     oracle.step([x], dtype="bf16", step=5, **dict(HP, lr=0.0))
     assert np.array_equal(x.master, p)
-    assert np.array_equal(x.weight_bf16, torch_bf16_bits(p))
+    assert np.array_equal(x.weight_out, torch_bf16_bits(p))
     assert np.mean(x.exp_avg != m) > 0.99 and np.mean(x.exp_avg_sq != v) > 0.99
 
 
@@ -399,13 +427,69 @@ def test_flag_and_propagation_of_non_finite_gradients(dtype, bad):
     x = make_tensor(p, np.zeros(n), np.zeros(n), grads)
     assert oracle.step([x], dtype=dtype, step=1, with_flag=True, **HP) == 1
     others = np.setdiff1d(np.arange(n), hit)
-    assert np.all(np.isnan(x.master[hit])) and np.all(x.weight_bf16[hit] == 0x7FC0)
+    assert np.all(np.isnan(x.master[hit])) and np.all(x.weight_out[hit] == 0x7FC0)
     if bad == "nan":
         assert np.all(np.isnan(x.exp_avg[hit]))
     else:
         assert np.all(np.isinf(x.exp_avg[hit])) and np.all(np.isinf(x.exp_avg_sq[hit]))
-    for f in ("master", "exp_avg", "exp_avg_sq", "weight_bf16"):
+    for f in ("master", "exp_avg", "exp_avg_sq", "weight_out"):
         assert np.array_equal(getattr(x, f)[others], getattr(clean, f)[others])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_gradient_check_finds_exactly_the_non_finite_aggregates(dtype):
+    rng = np.random.default_rng(21)
+    n, R = 3000, 3
+    big = {"bf16": 0x7F7F, "fp16": 0x7BFF}[dtype]      # largest finite
+    inf = {"bf16": 0x7F80, "fp16": 0x7C00}[dtype]
+    ninf = {"bf16": 0xFF80, "fp16": 0xFC00}[dtype]
+    nan = {"bf16": 0x7FC1, "fp16": 0x7E01}[dtype]
+    base = [random_bf16(rng, n) if dtype == "bf16" else
+            np.asarray(rng.standard_normal(n), np.float16).view(np.uint16) for _ in range(R)]
+    x = make_tensor(np.zeros(n), np.zeros(n), np.zeros(n), base)
+    assert oracle.check_finite([x], dtype=dtype) == 0
+    for code in (inf, ninf, nan):
+        g = [b.copy() for b in base]
+        g[1][n // 2] = code
+        assert oracle.check_finite([make_tensor(np.zeros(n), np.zeros(n), np.zeros(n), g)],
+                                   dtype=dtype) == 1
+    # +Inf + -Inf in two replicas sums to NaN
+    g = [b.copy() for b in base]
+    g[0][7], g[2][7] = inf, ninf
+    assert oracle.check_finite([make_tensor(np.zeros(n), np.zeros(n), np.zeros(n), g)],
+                               dtype=dtype) == 1
+    # finite replicas whose sum overflows FP32 only for BF16 (FP16's max is far below)
+    g = [np.full(n, big, np.uint16) for _ in range(R)]
+    want = 1 if dtype == "bf16" else 0
+    assert oracle.check_finite([make_tensor(np.zeros(n), np.zeros(n), np.zeros(n), g)],
+                               dtype=dtype) == want
+    # the unscale factor enters: 3 * 65504 * 2^112 ~ 2^129.6 overflows FP32
+    g = [np.full(n, 0x7BFF, np.uint16) for _ in range(R)]
+    if dtype == "fp16":
+        assert oracle.check_finite([make_tensor(np.zeros(n), np.zeros(n), np.zeros(n), g)],
+                                   dtype=dtype, unscale=2.0 ** 112) == 1
+
+
+def test_output_format_only_changes_the_compute_copy():
+    rng = np.random.default_rng(22)
+    n = 5000
+    p = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    m = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v = (rng.random(n) * 1e-6).astype(np.float32)
+    g = [random_bf16(rng, n), random_bf16(rng, n)]
+    outs = {}
+    for fmt in ("bf16", "fp16", "none"):
+        x = make_tensor(p, m, v, g)
+        x.weight_out[:] = 0x7FAA
+        oracle.step([x], dtype="bf16", step=4, out_dtype=fmt, **HP)
+        outs[fmt] = x
+    for f in ("master", "exp_avg", "exp_avg_sq"):
+        assert np.array_equal(getattr(outs["bf16"], f), getattr(outs["fp16"], f))
+        assert np.array_equal(getattr(outs["bf16"], f), getattr(outs["none"], f))
+    assert np.array_equal(outs["bf16"].weight_out, torch_bf16_bits(outs["bf16"].master))
+    assert np.array_equal(outs["fp16"].weight_out,
+                          outs["fp16"].master.astype(np.float16).view(np.uint16))
+    assert np.all(outs["none"].weight_out == 0x7FAA)
 
 
 def test_large_finite_fp16_sum_does_not_raise_the_flag():
@@ -421,12 +505,12 @@ def test_every_output_element_is_written():
     for n in sizes:
         x = make_tensor((rng.standard_normal(n) * 0.02).astype(np.float32), np.zeros(n),
                         np.zeros(n), [random_bf16(rng, n), random_bf16(rng, n)])
-        x.weight_bf16[:] = 0x7FAA  # a NaN payload the cast never produces
+        x.weight_out[:] = 0x7FAA  # a NaN payload the cast never produces
         ts.append(x)
     oracle.step(ts, dtype="bf16", step=1, **HP)
     for x in ts:
-        assert not np.any(x.weight_bf16 == 0x7FAA)
-        assert np.array_equal(x.weight_bf16, torch_bf16_bits(x.master))
+        assert not np.any(x.weight_out == 0x7FAA)
+        assert np.array_equal(x.weight_out, torch_bf16_bits(x.master))
 
 
 def test_invalid_hyperparameters_are_rejected():
