@@ -22,6 +22,8 @@
  *    (SlideFormer), technical summary 2.2: gradients in a BF16/FP16 buffer,
  *    FP32 -> BF16 conversion of the master for the compute copy, and
  *    preallocated fixed-size buffers (so the library allocates nothing).
+ *    "AutoHete" (mhpn.cn), section 2.2: on-the-fly FP32 -> FP16 conversion
+ *    (the FP16 compute copy).
  *  - The pages print no Adam formula. The update is PyTorch's AdamW, the
  *    optimizer of the FSDP2 runs SlideDP checks its loss against (section
  *    实验结果, results):
@@ -30,7 +32,8 @@
  *        v   = beta2*v + (1-beta2)*(g*g)
  *        p   = p*(1 - lr*weight_decay)
  *              - lr/(1-beta1^t) * m / (sqrt(v)/sqrt(1-beta2^t) + eps)
- *        w   = BF16(p), round to nearest, ties to even; NaN -> 0x7FC0
+ *        w   = BF16(p) or FP16(p), round to nearest, ties to even
+ *              (NaN -> 0x7FC0 / 0x7E00), or no compute copy at all
  *    in FP32, one rounding per operation and no fused multiply-add; the
  *    nine constants beta1, 1-beta1, beta2, 1-beta2, lr/(1-beta1^t),
  *    sqrt(1-beta2^t), eps, 1-lr*weight_decay and grad_unscale are computed
@@ -72,29 +75,38 @@ typedef enum {
 
 typedef enum { LA_GRAD_BF16 = 0, LA_GRAD_FP16 = 1 } la_grad_dtype;
 
+/* Format of the compute copy of the new master weights. */
+typedef enum { LA_OUT_BF16 = 0, LA_OUT_FP16 = 1, LA_OUT_NONE = 2 } la_out_dtype;
+
 /* One tensor of the layer. All arrays hold `numel` elements, contiguous.
- * master, exp_avg, exp_avg_sq are read and written in place; weight_bf16 is
- * written only (BF16 bit patterns); grads[0..R-1] are read only, in the
- * layer's gradient dtype. Gradient replicas may alias one another (passing
- * one buffer R times is legal); no written array may overlap any other array
- * of the call. numel == 0 tensors are skipped and their pointers ignored. */
+ * master, exp_avg, exp_avg_sq are read and written in place; weight_out is
+ * written only (BF16 or FP16 bit patterns, per the layer's out_dtype; not
+ * used, and may be NULL, with LA_OUT_NONE); grads[0..R-1] are read only, in
+ * the layer's gradient dtype. Gradient replicas may alias one another
+ * (passing one buffer R times is legal); no written array may overlap any
+ * other array of the call. numel == 0 tensors are skipped and their pointers
+ * ignored. */
 typedef struct {
   float *master;
   float *exp_avg;
   float *exp_avg_sq;
-  uint16_t *weight_bf16;
+  uint16_t *weight_out;
   const void *grads[LA_MAX_REPLICAS];
   int64_t numel;
 } la_tensor_desc;
 
 /* The layer: a host array of num_tensors descriptors (0 <= num_tensors <=
- * LA_MAX_TENSORS; 0 is a no-op), the number of replicas R and their dtype
- * (la_grad_dtype). The descriptor array is read during the call only. */
+ * LA_MAX_TENSORS; 0 is a no-op), the number of replicas R, their dtype
+ * (la_grad_dtype) and the compute-copy format (la_out_dtype). The layer's
+ * elements are numbered 0..N-1 across its tensors in order (tensor 0 first);
+ * the range entry point uses that numbering. The descriptor array is read
+ * during the call only. */
 typedef struct {
   const la_tensor_desc *tensors;
   int32_t num_tensors;
   int32_t num_replicas;
   int32_t grad_dtype;
+  int32_t out_dtype;
 } la_layer_desc;
 
 /* Hyperparameters of one step. step is the 1-based count of the update being
@@ -129,6 +141,45 @@ LA_API la_status layer_adam_step(const la_layer_desc *layer,
                                  const la_adam_params *hp,
                                  int32_t *overflow_flag, void *hip_stream);
 
+/* The same update restricted to the layer's elements [elem_begin, elem_end)
+ * (0 <= elem_begin <= elem_end <= N, numbering as in la_layer_desc). Calls
+ * over a partition of [0, N) leave exactly the state one layer_adam_step
+ * leaves, bit for bit: the update is elementwise. This is the per-chunk
+ * release of "SlideDP: Scaling Host-Resident LLM Fine-Tuning Across Multiple
+ * GPUs", sections 核心方法 and 方法步骤详情 (a chunk of the layer is updated
+ * as soon as its reduced gradient is ready); a caller overlapping the update
+ * with the gradient's producer makes the update stream wait on the
+ * producer's event per chunk. Arguments are checked as for layer_adam_step
+ * (the whole layer's buffers), plus the range. */
+LA_API la_status layer_adam_step_range(const la_layer_desc *layer,
+                                       const la_adam_params *hp,
+                                       int64_t elem_begin, int64_t elem_end,
+                                       int32_t *overflow_flag, void *hip_stream);
+
+/* Pre-pass for overflow-gated steps: sets *found_nonfinite (a 4-byte-aligned
+ * int32 in device memory) to 1 if some aggregated gradient element of the
+ * layer -- the left-to-right sum of its R replicas times grad_unscale, in
+ * FP32, exactly as the update forms it -- is +-Inf or NaN. Never clears it.
+ * Reads only the gradients, 2R bytes per parameter; it may stop reading
+ * once it sees the flag already set. grad_unscale must be finite and > 0. */
+LA_API la_status la_check_gradients(const la_layer_desc *layer,
+                                    double grad_unscale,
+                                    int32_t *found_nonfinite,
+                                    void *hip_stream);
+
+/* layer_adam_step that does nothing -- no state, compute copy or flag is
+ * touched -- when the device int32 *skip_if_nonzero (4-byte aligned; may not
+ * be NULL) holds a non-zero value when the kernel runs. With
+ * la_check_gradients writing that flag for every layer first, a step whose
+ * gradients overflowed is skipped without a host synchronisation (the usual
+ * mixed-precision loss-scaling rule). The caller decides from the same flag,
+ * once read, whether to count the step in t. */
+LA_API la_status layer_adam_step_gated(const la_layer_desc *layer,
+                                       const la_adam_params *hp,
+                                       const int32_t *skip_if_nonzero,
+                                       int32_t *overflow_flag,
+                                       void *hip_stream);
+
 /* Bytes of mixed-precision Adam state the layer stands for: 16 per
  * parameter (2 BF16 weight + 2 gradient + 4 FP32 master + 8 FP32 m and v).
  * -1 if the descriptor is invalid. Host only. */
@@ -136,7 +187,8 @@ LA_API int64_t la_state_bytes(const la_layer_desc *layer);
 
 /* Bytes one layer_adam_step moves to and from HBM in the ideal case:
  * (2R + 26) per parameter = R gradient reads + master, m, v read and written
- * + the BF16 write. -1 if the descriptor is invalid. Host only. */
+ * + the 2-byte compute copy ((2R + 24) with LA_OUT_NONE). -1 if the
+ * descriptor is invalid. Host only. */
 LA_API int64_t la_traffic_bytes(const la_layer_desc *layer);
 
 /* Message of the calling thread's last failed call ("" if none). The pointer

@@ -26,9 +26,11 @@ LA_OK = 0
 STATUS_NAMES = {0: "LA_OK", 1: "LA_ERR_INVALID_ARGUMENT", 2: "LA_ERR_MISALIGNED",
                 3: "LA_ERR_ALIASING", 4: "LA_ERR_UNSUPPORTED", 5: "LA_ERR_HIP"}
 GRAD_BF16, GRAD_FP16 = 0, 1
+OUT_BF16, OUT_FP16, OUT_NONE = 0, 1, 2
 
 # Exported symbols, as declared in include/layeradam.h.
-EXPORTS = ("layer_adam_step", "la_state_bytes", "la_traffic_bytes", "la_last_error",
+EXPORTS = ("layer_adam_step", "layer_adam_step_range", "layer_adam_step_gated",
+           "la_check_gradients", "la_state_bytes", "la_traffic_bytes", "la_last_error",
            "la_version")
 
 
@@ -36,7 +38,7 @@ class TensorDesc(ctypes.Structure):
     _fields_ = [("master", ctypes.c_void_p),
                 ("exp_avg", ctypes.c_void_p),
                 ("exp_avg_sq", ctypes.c_void_p),
-                ("weight_bf16", ctypes.c_void_p),
+                ("weight_out", ctypes.c_void_p),
                 ("grads", ctypes.c_void_p * MAX_REPLICAS),
                 ("numel", ctypes.c_int64)]
 
@@ -45,7 +47,8 @@ class LayerDesc(ctypes.Structure):
     _fields_ = [("tensors", ctypes.POINTER(TensorDesc)),
                 ("num_tensors", ctypes.c_int32),
                 ("num_replicas", ctypes.c_int32),
-                ("grad_dtype", ctypes.c_int32)]
+                ("grad_dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32)]
 
 
 class AdamParams(ctypes.Structure):
@@ -99,6 +102,16 @@ def load(path: Optional[str] = None):
     lib.layer_adam_step.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(AdamParams),
                                     ctypes.c_void_p, ctypes.c_void_p]
     lib.layer_adam_step.restype = ctypes.c_int
+    lib.layer_adam_step_range.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(AdamParams),
+                                          ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                          ctypes.c_void_p]
+    lib.layer_adam_step_range.restype = ctypes.c_int
+    lib.layer_adam_step_gated.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(AdamParams),
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.layer_adam_step_gated.restype = ctypes.c_int
+    lib.la_check_gradients.argtypes = [ctypes.POINTER(LayerDesc), ctypes.c_double,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+    lib.la_check_gradients.restype = ctypes.c_int
     lib.la_state_bytes.argtypes = [ctypes.POINTER(LayerDesc)]
     lib.la_state_bytes.restype = ctypes.c_int64
     lib.la_traffic_bytes.argtypes = [ctypes.POINTER(LayerDesc)]
@@ -124,20 +137,21 @@ def last_error() -> str:
 # ---------------------------------------------------------------------------
 # Raw descriptors (plain integers as pointers)
 # ---------------------------------------------------------------------------
-def make_layer(tensors: Sequence[dict], num_replicas: int, grad_dtype: int):
+def make_layer(tensors: Sequence[dict], num_replicas: int, grad_dtype: int,
+               out_dtype: int = OUT_BF16):
     """Build a LayerDesc from dicts with integer pointers: master, exp_avg,
-    exp_avg_sq, weight_bf16, grads (list of R), numel. Returns (desc, keepalive)."""
+    exp_avg_sq, weight_out, grads (list of R), numel. Returns (desc, keepalive)."""
     arr = (TensorDesc * max(1, len(tensors)))()
     for i, t in enumerate(tensors):
         arr[i].master = t.get("master") or 0
         arr[i].exp_avg = t.get("exp_avg") or 0
         arr[i].exp_avg_sq = t.get("exp_avg_sq") or 0
-        arr[i].weight_bf16 = t.get("weight_bf16") or 0
+        arr[i].weight_out = t.get("weight_out") or 0
         for r, g in enumerate(t.get("grads", ())):
             arr[i].grads[r] = g or 0
         arr[i].numel = int(t["numel"])
     desc = LayerDesc(ctypes.cast(arr, ctypes.POINTER(TensorDesc)), len(tensors),
-                     num_replicas, grad_dtype)
+                     num_replicas, grad_dtype, out_dtype)
     return desc, arr
 
 
@@ -146,14 +160,42 @@ def make_params(lr, beta1, beta2, eps, weight_decay, step, grad_unscale=1.0) -> 
                       float(weight_decay), int(step), float(grad_unscale))
 
 
-def step_raw(desc: LayerDesc, params: AdamParams, overflow_flag: int = 0,
-             stream: int = 0) -> None:
-    """Call layer_adam_step on raw descriptors; raise LayerAdamError on failure."""
-    lib = load()
-    rc = lib.layer_adam_step(ctypes.byref(desc), ctypes.byref(params),
-                             overflow_flag or None, stream or None)
+def _raise_on(rc: int, lib) -> None:
     if rc != LA_OK:
         raise LayerAdamError(rc, lib.la_last_error().decode())
+
+
+def step_raw(desc: LayerDesc, params: AdamParams, overflow_flag: int = 0,
+             stream: int = 0) -> None:
+    """layer_adam_step on raw descriptors; raises LayerAdamError on failure."""
+    lib = load()
+    _raise_on(lib.layer_adam_step(ctypes.byref(desc), ctypes.byref(params),
+                                  overflow_flag or None, stream or None), lib)
+
+
+def step_range_raw(desc: LayerDesc, params: AdamParams, begin: int, end: int,
+                   overflow_flag: int = 0, stream: int = 0) -> None:
+    """layer_adam_step_range on raw descriptors."""
+    lib = load()
+    _raise_on(lib.layer_adam_step_range(ctypes.byref(desc), ctypes.byref(params), int(begin),
+                                        int(end), overflow_flag or None, stream or None), lib)
+
+
+def step_gated_raw(desc: LayerDesc, params: AdamParams, skip_if_nonzero: int,
+                   overflow_flag: int = 0, stream: int = 0) -> None:
+    """layer_adam_step_gated on raw descriptors."""
+    lib = load()
+    _raise_on(lib.layer_adam_step_gated(ctypes.byref(desc), ctypes.byref(params),
+                                        skip_if_nonzero or None, overflow_flag or None,
+                                        stream or None), lib)
+
+
+def check_gradients_raw(desc: LayerDesc, grad_unscale: float, found_nonfinite: int,
+                        stream: int = 0) -> None:
+    """la_check_gradients on raw descriptors."""
+    lib = load()
+    _raise_on(lib.la_check_gradients(ctypes.byref(desc), float(grad_unscale),
+                                     found_nonfinite or None, stream or None), lib)
 
 
 def state_bytes_raw(desc: LayerDesc) -> int:
@@ -177,34 +219,72 @@ def _grad_dtype_of(grads) -> int:
     raise TypeError(f"gradients must all be bfloat16 or all float16, got {kinds}")
 
 
-def _describe(params, grads):
+def _out_dtype_of(params) -> int:
+    import torch
+    kinds = {x[3].dtype if len(x) > 3 and x[3] is not None else None for x in params}
+    if kinds <= {torch.bfloat16}:
+        return OUT_BF16
+    if kinds <= {torch.float16}:
+        return OUT_FP16
+    if kinds == {None}:
+        return OUT_NONE
+    raise TypeError(f"compute copies must all be bfloat16, all float16 or all None, got {kinds}")
+
+
+def _describe(params, grads, need_state: bool = True):
     import torch
     if len(params) != len(grads):
         raise ValueError("one list of gradient replicas per tensor")
-    if not params:
-        return [], 1, GRAD_BF16
+    if not grads:
+        return [], 1, GRAD_BF16, OUT_BF16
     R = len(grads[0])
     gd = _grad_dtype_of(grads)
+    od = _out_dtype_of(params) if need_state else OUT_NONE
     out = []
-    for i, ((p, m, v, w), gs) in enumerate(zip(params, grads)):
-        n = p.numel()
-        for name, x, dt in (("master", p, torch.float32), ("exp_avg", m, torch.float32),
-                            ("exp_avg_sq", v, torch.float32),
-                            ("weight_bf16", w, torch.bfloat16)):
-            if x.dtype != dt and not (name == "weight_bf16" and x.dtype in (torch.int16,)):
-                raise TypeError(f"tensor {i}: {name} must be {dt}, got {x.dtype}")
-            if x.numel() != n or not x.is_contiguous() or not x.is_cuda:
-                raise ValueError(f"tensor {i}: {name} must be a contiguous CUDA tensor "
-                                 f"of {n} elements")
+    for i, (x, gs) in enumerate(zip(params, grads)):
+        n = gs[0].numel() if gs else 0
+        d = {"numel": n}
+        if need_state:
+            p, m, v = x[0], x[1], x[2]
+            w = x[3] if len(x) > 3 else None
+            n = p.numel()
+            d["numel"] = n
+            for name, t in (("master", p), ("exp_avg", m), ("exp_avg_sq", v)):
+                if t.dtype != torch.float32:
+                    raise TypeError(f"tensor {i}: {name} must be float32, got {t.dtype}")
+                if t.numel() != n or not t.is_contiguous() or not t.is_cuda:
+                    raise ValueError(f"tensor {i}: {name} must be a contiguous CUDA tensor "
+                                     f"of {n} elements")
+                d[name] = t.data_ptr()
+            if w is not None:
+                if w.numel() != n or not w.is_contiguous() or not w.is_cuda:
+                    raise ValueError(f"tensor {i}: the compute copy must be a contiguous CUDA "
+                                     f"tensor of {n} elements")
+                d["weight_out"] = w.data_ptr()
         if len(gs) != R:
             raise ValueError(f"tensor {i}: {len(gs)} gradient replicas, expected {R}")
         for g in gs:
             if g.numel() != n or not g.is_contiguous() or not g.is_cuda:
                 raise ValueError(f"tensor {i}: gradients must be contiguous CUDA tensors "
                                  f"of {n} elements")
-        out.append(dict(master=p.data_ptr(), exp_avg=m.data_ptr(), exp_avg_sq=v.data_ptr(),
-                        weight_bf16=w.data_ptr(), grads=[g.data_ptr() for g in gs], numel=n))
-    return out, R, gd
+        d["grads"] = [g.data_ptr() for g in gs]
+        out.append(d)
+    return out, R, gd, od
+
+
+def _flag_ptr(flag) -> int:
+    import torch
+    if flag is None:
+        return 0
+    if flag.dtype != torch.int32 or not flag.is_cuda:
+        raise TypeError("flags must be int32 CUDA tensors")
+    return flag.data_ptr()
+
+
+def _stream_ptr(stream) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
 
 
 def step(params, grads, *, lr: float, beta1: float, beta2: float, eps: float,
@@ -214,22 +294,52 @@ def step(params, grads, *, lr: float, beta1: float, beta2: float, eps: float,
     current torch stream).
 
     params: per tensor a tuple (master fp32, exp_avg fp32, exp_avg_sq fp32,
-            weight_bf16 bf16), updated/written in place.
+            compute copy), updated/written in place; the compute copy is a
+            bfloat16 or float16 tensor (the same for every tensor), or None
+            for no copy.
     grads:  per tensor a list of R gradient replicas (all bf16 or all fp16).
     overflow_flag: optional int32 CUDA tensor of one element (set to 1 on a
             non-finite aggregated gradient; never cleared).
     """
-    import torch
-    tensors, R, gd = _describe(params, grads)
-    desc, keep = make_layer(tensors, R, gd)
+    tensors, R, gd, od = _describe(params, grads)
+    desc, keep = make_layer(tensors, R, gd, od)
     hp = make_params(lr, beta1, beta2, eps, weight_decay, step, grad_unscale)
-    flag_ptr = 0
-    if overflow_flag is not None:
-        if overflow_flag.dtype != torch.int32 or not overflow_flag.is_cuda:
-            raise TypeError("overflow_flag must be an int32 CUDA tensor")
-        flag_ptr = overflow_flag.data_ptr()
-    s = stream if stream is not None else torch.cuda.current_stream()
-    step_raw(desc, hp, flag_ptr, s.cuda_stream)
+    step_raw(desc, hp, _flag_ptr(overflow_flag), _stream_ptr(stream))
+    del keep
+
+
+def step_range(params, grads, begin: int, end: int, *, lr: float, beta1: float, beta2: float,
+               eps: float, weight_decay: float, step: int, grad_unscale: float = 1.0,
+               overflow_flag=None, stream=None) -> None:
+    """The update of the layer's elements [begin, end) only (elements
+    numbered across the tensors in order)."""
+    tensors, R, gd, od = _describe(params, grads)
+    desc, keep = make_layer(tensors, R, gd, od)
+    hp = make_params(lr, beta1, beta2, eps, weight_decay, step, grad_unscale)
+    step_range_raw(desc, hp, begin, end, _flag_ptr(overflow_flag), _stream_ptr(stream))
+    del keep
+
+
+def step_gated(params, grads, skip_if_nonzero, *, lr: float, beta1: float, beta2: float,
+               eps: float, weight_decay: float, step: int, grad_unscale: float = 1.0,
+               overflow_flag=None, stream=None) -> None:
+    """The update, or nothing at all if the int32 CUDA scalar
+    ``skip_if_nonzero`` holds a non-zero value when the kernel runs."""
+    tensors, R, gd, od = _describe(params, grads)
+    desc, keep = make_layer(tensors, R, gd, od)
+    hp = make_params(lr, beta1, beta2, eps, weight_decay, step, grad_unscale)
+    step_gated_raw(desc, hp, _flag_ptr(skip_if_nonzero), _flag_ptr(overflow_flag),
+                   _stream_ptr(stream))
+    del keep
+
+
+def check_gradients(grads, found_nonfinite, *, grad_unscale: float = 1.0, stream=None) -> None:
+    """Set the int32 CUDA scalar ``found_nonfinite`` to 1 if some aggregated
+    gradient (sum of the replicas times grad_unscale) is non-finite.
+    grads: per tensor a list of R replicas."""
+    tensors, R, gd, _ = _describe([None] * len(grads), grads, need_state=False)
+    desc, keep = make_layer(tensors, R, gd, OUT_NONE)
+    check_gradients_raw(desc, grad_unscale, _flag_ptr(found_nonfinite), _stream_ptr(stream))
     del keep
 
 
@@ -239,7 +349,8 @@ def state_bytes(numels: Sequence[int], num_replicas: int = 1) -> int:
     return state_bytes_raw(desc)
 
 
-def traffic_bytes(numels: Sequence[int], num_replicas: int) -> int:
-    """(2R + 26) bytes per parameter (la_traffic_bytes)."""
-    desc, keep = make_layer([dict(numel=n) for n in numels], num_replicas, GRAD_BF16)
+def traffic_bytes(numels: Sequence[int], num_replicas: int, out_dtype: int = OUT_BF16) -> int:
+    """(2R + 26) bytes per parameter, (2R + 24) without a compute copy
+    (la_traffic_bytes)."""
+    desc, keep = make_layer([dict(numel=n) for n in numels], num_replicas, GRAD_BF16, out_dtype)
     return traffic_bytes_raw(desc)

@@ -1,8 +1,9 @@
 // la_api.cpp -- the C ABI of liblayeradam.so (declared in include/layeradam.h).
 //
 // Host side only: checks every argument before anything is enqueued, derives
-// the FP32 constants of the step, splits the layer into launches of at most
-// kTensorsPerLaunch tensors and enqueues them on the caller's stream.
+// the FP32 constants of the step, turns the layer (or an element range of it)
+// into kernel tensor entries, splits them into launches of at most
+// kTensorsPerLaunch entries and enqueues them on the caller's stream.
 
 #include <hip/hip_runtime.h>
 
@@ -13,7 +14,6 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
-#include <utility>
 #include <vector>
 
 #include "la_internal.h"
@@ -80,15 +80,11 @@ constexpr int kMaxGrid = 1 << 30;
 
 bool finite_nonneg(double x) { return std::isfinite(x) && x >= 0.0; }
 
-struct Range {
-  uintptr_t begin, end;  // [begin, end)
-  const char* what;
-  int tensor;
-};
+bool aligned(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
-bool overlaps(const Range& a, const Range& b) { return a.begin < b.end && b.begin < a.end; }
+enum class Mode { kUpdate, kCheck };
 
-// Counts, dtype and sizes; no pointers (enough for the byte accounting).
+// Counts, dtypes and sizes; no pointers (enough for the byte accounting).
 la_status check_counts(const la_layer_desc* layer) {
   if (layer == nullptr) return fail(LA_ERR_INVALID_ARGUMENT, "layer descriptor is NULL");
   if (layer->num_tensors < 0 || layer->num_tensors > LA_MAX_TENSORS)
@@ -103,6 +99,10 @@ la_status check_counts(const la_layer_desc* layer) {
   if (layer->grad_dtype != LA_GRAD_BF16 && layer->grad_dtype != LA_GRAD_FP16)
     return fail(LA_ERR_UNSUPPORTED, "grad_dtype = %d, need LA_GRAD_BF16 or LA_GRAD_FP16",
                 layer->grad_dtype);
+  if (layer->out_dtype != LA_OUT_BF16 && layer->out_dtype != LA_OUT_FP16 &&
+      layer->out_dtype != LA_OUT_NONE)
+    return fail(LA_ERR_UNSUPPORTED, "out_dtype = %d, need LA_OUT_BF16, LA_OUT_FP16 or LA_OUT_NONE",
+                layer->out_dtype);
   // Largest numel whose byte sizes and (2R + 26)-byte traffic stay far from
   // overflowing 64 bits, even summed over LA_MAX_TENSORS tensors.
   constexpr int64_t kMaxNumel = int64_t(1) << 48;
@@ -115,36 +115,53 @@ la_status check_counts(const la_layer_desc* layer) {
   return LA_OK;
 }
 
-la_status check_layer(const la_layer_desc* layer) {
-  la_status st = check_counts(layer);
-  if (st != LA_OK) return st;
+// Every buffer the mode touches: present and 16-byte aligned.
+la_status check_pointers(const la_layer_desc* layer, Mode mode) {
+  const bool state = mode == Mode::kUpdate;
+  const bool out = state && layer->out_dtype != LA_OUT_NONE;
   for (int i = 0; i < layer->num_tensors; ++i) {
     const la_tensor_desc& t = layer->tensors[i];
     if (t.numel == 0) continue;
-    const void* ptrs[4 + LA_MAX_REPLICAS] = {t.master, t.exp_avg, t.exp_avg_sq, t.weight_bf16};
-    const char* names[4] = {"master", "exp_avg", "exp_avg_sq", "weight_bf16"};
-    for (int r = 0; r < layer->num_replicas; ++r) ptrs[4 + r] = t.grads[r];
+    struct {
+      const void* p;
+      const char* name;
+      bool used;
+    } bufs[4 + LA_MAX_REPLICAS] = {{t.master, "master", state},
+                                   {t.exp_avg, "exp_avg", state},
+                                   {t.exp_avg_sq, "exp_avg_sq", state},
+                                   {t.weight_out, "weight_out", out}};
+    for (int r = 0; r < layer->num_replicas; ++r) bufs[4 + r] = {t.grads[r], "grads[r]", true};
     for (int k = 0; k < 4 + layer->num_replicas; ++k) {
-      const char* name = k < 4 ? names[k] : "grads";
-      if (ptrs[k] == nullptr)
-        return fail(LA_ERR_INVALID_ARGUMENT, "tensor %d: %s%s is NULL", i, name,
-                    k < 4 ? "" : "[r]");
-      if (reinterpret_cast<uintptr_t>(ptrs[k]) % LA_ALIGNMENT != 0)
-        return fail(LA_ERR_MISALIGNED, "tensor %d: %s%s is not %d-byte aligned", i, name,
-                    k < 4 ? "" : "[r]", LA_ALIGNMENT);
+      if (!bufs[k].used) continue;
+      if (bufs[k].p == nullptr)
+        return fail(LA_ERR_INVALID_ARGUMENT, "tensor %d: %s is NULL", i, bufs[k].name);
+      if (!aligned(bufs[k].p, LA_ALIGNMENT))
+        return fail(LA_ERR_MISALIGNED, "tensor %d: %s is not %d-byte aligned", i, bufs[k].name,
+                    LA_ALIGNMENT);
     }
   }
   return LA_OK;
 }
 
-// Written ranges must be pairwise disjoint and must not overlap any gradient
-// or the flag. Sort the written ranges; check neighbours, then look every
-// gradient range up by binary search.
-la_status check_aliasing(const la_layer_desc* layer, const int32_t* flag) {
+struct Range {
+  uintptr_t begin, end;  // [begin, end)
+  const char* what;
+  int tensor;
+};
+
+bool overlaps(const Range& a, const Range& b) { return a.begin < b.end && b.begin < a.end; }
+
+// Written ranges must be pairwise disjoint and must not overlap any range
+// that is only read (gradients, the skip flag). Sort the written ranges;
+// check neighbours, then look every read range up by binary search.
+la_status check_aliasing(const la_layer_desc* layer, Mode mode, const int32_t* flag,
+                         const int32_t* skip) {
   std::vector<Range> written;
   std::vector<Range> read;
+  const bool state = mode == Mode::kUpdate;
+  const bool out = state && layer->out_dtype != LA_OUT_NONE;
   written.reserve(4 * layer->num_tensors + 1);
-  read.reserve(layer->num_replicas * layer->num_tensors);
+  read.reserve(layer->num_replicas * layer->num_tensors + 1);
   for (int i = 0; i < layer->num_tensors; ++i) {
     const la_tensor_desc& t = layer->tensors[i];
     if (t.numel == 0) continue;
@@ -153,15 +170,21 @@ la_status check_aliasing(const la_layer_desc* layer, const int32_t* flag) {
       const uintptr_t b = reinterpret_cast<uintptr_t>(p);
       v.push_back({b, b + bytes, what, i});
     };
-    add(written, t.master, 4 * n, "master");
-    add(written, t.exp_avg, 4 * n, "exp_avg");
-    add(written, t.exp_avg_sq, 4 * n, "exp_avg_sq");
-    add(written, t.weight_bf16, 2 * n, "weight_bf16");
+    if (state) {
+      add(written, t.master, 4 * n, "master");
+      add(written, t.exp_avg, 4 * n, "exp_avg");
+      add(written, t.exp_avg_sq, 4 * n, "exp_avg_sq");
+    }
+    if (out) add(written, t.weight_out, 2 * n, "weight_out");
     for (int r = 0; r < layer->num_replicas; ++r) add(read, t.grads[r], 2 * n, "grads");
   }
   if (flag != nullptr) {
     const uintptr_t b = reinterpret_cast<uintptr_t>(flag);
-    written.push_back({b, b + 4, "overflow_flag", -1});
+    written.push_back({b, b + 4, "the flag", -1});
+  }
+  if (skip != nullptr) {
+    const uintptr_t b = reinterpret_cast<uintptr_t>(skip);
+    read.push_back({b, b + 4, "skip_if_nonzero", -1});
   }
   std::sort(written.begin(), written.end(),
             [](const Range& a, const Range& b) { return a.begin < b.begin; });
@@ -172,14 +195,20 @@ la_status check_aliasing(const la_layer_desc* layer, const int32_t* flag) {
                   written[k].tensor);
   }
   for (const Range& g : read) {
-    // first written range that ends after g begins
+    // first written range that ends after g begins (written ranges are
+    // disjoint and sorted, so their ends are sorted too)
     auto it = std::lower_bound(written.begin(), written.end(), g.begin,
                                [](const Range& w, uintptr_t x) { return w.end <= x; });
-    // written ranges are disjoint and sorted, so their ends are sorted too
     if (it != written.end() && overlaps(*it, g))
-      return fail(LA_ERR_ALIASING, "a gradient of tensor %d overlaps %s of tensor %d", g.tensor,
+      return fail(LA_ERR_ALIASING, "%s of tensor %d overlaps %s of tensor %d", g.what, g.tensor,
                   it->what, it->tensor);
   }
+  return LA_OK;
+}
+
+la_status check_unscale(double u) {
+  if (!(std::isfinite(u) && u > 0.0))
+    return fail(LA_ERR_INVALID_ARGUMENT, "grad_unscale = %g, need finite > 0", u);
   return LA_OK;
 }
 
@@ -196,9 +225,8 @@ la_status derive_scalars(const la_adam_params* hp, la::Scalars* s) {
   if (!finite_nonneg(hp->eps)) return fail(LA_ERR_INVALID_ARGUMENT, "eps = %g", hp->eps);
   if (!finite_nonneg(hp->weight_decay))
     return fail(LA_ERR_INVALID_ARGUMENT, "weight_decay = %g", hp->weight_decay);
-  if (!(std::isfinite(hp->grad_unscale) && hp->grad_unscale > 0.0))
-    return fail(LA_ERR_INVALID_ARGUMENT, "grad_unscale = %g, need finite > 0",
-                hp->grad_unscale);
+  la_status st = check_unscale(hp->grad_unscale);
+  if (st != LA_OK) return st;
   // Bias corrections of AdamW at the 1-based step t, in double; each FP32
   // constant is rounded once.
   const double t = static_cast<double>(hp->step);
@@ -216,28 +244,26 @@ la_status derive_scalars(const la_adam_params* hp, la::Scalars* s) {
   return LA_OK;
 }
 
-}  // namespace
+int64_t total_numel(const la_layer_desc* layer) {
+  int64_t n = 0;
+  for (int i = 0; i < layer->num_tensors; ++i) n += layer->tensors[i].numel;
+  return n;
+}
 
-extern "C" {
-
-LA_API la_status layer_adam_step(const la_layer_desc* layer, const la_adam_params* hp,
-                                 int32_t* overflow_flag, void* hip_stream) {
-  la_status st = check_layer(layer);
-  if (st != LA_OK) return st;
-  la::Scalars s;
-  st = derive_scalars(hp, &s);
-  if (st != LA_OK) return st;
-  if (overflow_flag != nullptr && reinterpret_cast<uintptr_t>(overflow_flag) % 4 != 0)
-    return fail(LA_ERR_MISALIGNED, "overflow_flag is not 4-byte aligned");
-  st = check_aliasing(layer, overflow_flag);
-  if (st != LA_OK) return st;
-
-  // Non-empty tensors, in order.
+// Collect the kernel entries of elements [begin, end) and launch them in
+// batches. Within a tensor the sub-range starts at element s: the part before
+// the next multiple of 8 (at most 7 elements, so always the element-wise
+// path of the kernel) becomes its own entry, and the rest starts 16-byte
+// aligned (32 bytes into FP32 arrays, 16 into 16-bit arrays).
+la_status enqueue(const la_layer_desc* layer, Mode mode, const la::Scalars& s, int64_t begin,
+                  int64_t end, int32_t* flag, const int32_t* skip, void* hip_stream) {
   la::TensorArgs batch[la::kTensorsPerLaunch];
   int pending = 0;
   int launches = 0;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   la::LaunchShape shape{0, 0};
+  const bool fp16 = layer->grad_dtype == LA_GRAD_FP16;
+  const bool out = mode == Mode::kUpdate && layer->out_dtype != LA_OUT_NONE;
 
   auto flush = [&]() -> la_status {
     if (pending == 0) return LA_OK;
@@ -249,55 +275,133 @@ LA_API la_status layer_adam_step(const la_layer_desc* layer, const la_adam_param
       shape.grid_cap = kMaxGrid;
       shape.lds_bytes = lds_reserve(device, workgroups_per_cu());
     }
-    hipError_t e = la::launch_layer_adam(batch, pending, layer->num_replicas,
-                                         layer->grad_dtype == LA_GRAD_FP16, s, overflow_flag,
-                                         stream, shape);
+    hipError_t e = mode == Mode::kUpdate
+                       ? la::launch_layer_adam(batch, pending, layer->num_replicas, fp16,
+                                               layer->out_dtype, s, flag, skip, stream, shape)
+                       : la::launch_check_gradients(batch, pending, layer->num_replicas, fp16,
+                                                    s.u, flag, stream, shape);
     if (e != hipSuccess)
       return fail(LA_ERR_HIP, "kernel launch %d failed: %s", launches, hipGetErrorString(e));
     ++launches;
     pending = 0;
     return LA_OK;
   };
+  auto add = [&](const la_tensor_desc& t, int64_t first, int64_t count) -> la_status {
+    la::TensorArgs& a = batch[pending++];
+    const bool state = mode == Mode::kUpdate;
+    a.p = state ? t.master + first : nullptr;
+    a.m = state ? t.exp_avg + first : nullptr;
+    a.v = state ? t.exp_avg_sq + first : nullptr;
+    a.w = out ? t.weight_out + first : nullptr;
+    for (int r = 0; r < la::kMaxReplicas; ++r)
+      a.g[r] = r < layer->num_replicas ? static_cast<const uint16_t*>(t.grads[r]) + first
+                                       : nullptr;
+    a.numel = count;
+    return pending == la::kTensorsPerLaunch ? flush() : LA_OK;
+  };
 
+  int64_t offset = 0;  // layer element number of the tensor's first element
   for (int i = 0; i < layer->num_tensors; ++i) {
     const la_tensor_desc& t = layer->tensors[i];
-    if (t.numel == 0) continue;
-    la::TensorArgs& a = batch[pending++];
-    a.p = t.master;
-    a.m = t.exp_avg;
-    a.v = t.exp_avg_sq;
-    a.w = t.weight_bf16;
-    for (int r = 0; r < la::kMaxReplicas; ++r)
-      a.g[r] = r < layer->num_replicas ? static_cast<const uint16_t*>(t.grads[r]) : nullptr;
-    a.numel = t.numel;
-    if (pending == la::kTensorsPerLaunch) {
-      st = flush();
-      if (st != LA_OK) return st;
+    const int64_t lo = std::max(begin, offset), hi = std::min(end, offset + t.numel);
+    offset += t.numel;
+    if (lo >= hi) continue;
+    int64_t first = lo - offset + t.numel;  // element within the tensor
+    int64_t count = hi - lo;
+    const int64_t head = std::min(count, (8 - first % 8) % 8);
+    la_status st;
+    if (head > 0) {
+      if ((st = add(t, first, head)) != LA_OK) return st;
+      first += head;
+      count -= head;
     }
+    if (count > 0 && (st = add(t, first, count)) != LA_OK) return st;
   }
-  st = flush();
+  la_status st = flush();
   if (st != LA_OK) return st;
   return ok();
 }
 
+la_status update(const la_layer_desc* layer, const la_adam_params* hp, int64_t begin,
+                 int64_t end, bool whole, int32_t* flag, const int32_t* skip,
+                 void* hip_stream) {
+  la_status st = check_counts(layer);
+  if (st != LA_OK) return st;
+  if ((st = check_pointers(layer, Mode::kUpdate)) != LA_OK) return st;
+  la::Scalars s;
+  if ((st = derive_scalars(hp, &s)) != LA_OK) return st;
+  if (flag != nullptr && !aligned(flag, 4))
+    return fail(LA_ERR_MISALIGNED, "overflow_flag is not 4-byte aligned");
+  if (skip != nullptr && !aligned(skip, 4))
+    return fail(LA_ERR_MISALIGNED, "skip_if_nonzero is not 4-byte aligned");
+  const int64_t n = total_numel(layer);
+  if (whole) {
+    begin = 0;
+    end = n;
+  } else if (begin < 0 || begin > end || end > n) {
+    return fail(LA_ERR_INVALID_ARGUMENT, "element range [%lld, %lld) outside [0, %lld]",
+                static_cast<long long>(begin), static_cast<long long>(end),
+                static_cast<long long>(n));
+  }
+  if ((st = check_aliasing(layer, Mode::kUpdate, flag, skip)) != LA_OK) return st;
+  return enqueue(layer, Mode::kUpdate, s, begin, end, flag, skip, hip_stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+LA_API la_status layer_adam_step(const la_layer_desc* layer, const la_adam_params* hp,
+                                 int32_t* overflow_flag, void* hip_stream) {
+  return update(layer, hp, 0, 0, true, overflow_flag, nullptr, hip_stream);
+}
+
+LA_API la_status layer_adam_step_range(const la_layer_desc* layer, const la_adam_params* hp,
+                                       int64_t elem_begin, int64_t elem_end,
+                                       int32_t* overflow_flag, void* hip_stream) {
+  return update(layer, hp, elem_begin, elem_end, false, overflow_flag, nullptr, hip_stream);
+}
+
+LA_API la_status layer_adam_step_gated(const la_layer_desc* layer, const la_adam_params* hp,
+                                       const int32_t* skip_if_nonzero,
+                                       int32_t* overflow_flag, void* hip_stream) {
+  if (skip_if_nonzero == nullptr)
+    return fail(LA_ERR_INVALID_ARGUMENT, "skip_if_nonzero is NULL");
+  return update(layer, hp, 0, 0, true, overflow_flag, skip_if_nonzero, hip_stream);
+}
+
+LA_API la_status la_check_gradients(const la_layer_desc* layer, double grad_unscale,
+                                    int32_t* found_nonfinite, void* hip_stream) {
+  la_status st = check_counts(layer);
+  if (st != LA_OK) return st;
+  if ((st = check_pointers(layer, Mode::kCheck)) != LA_OK) return st;
+  if ((st = check_unscale(grad_unscale)) != LA_OK) return st;
+  if (found_nonfinite == nullptr)
+    return fail(LA_ERR_INVALID_ARGUMENT, "found_nonfinite is NULL");
+  if (!aligned(found_nonfinite, 4))
+    return fail(LA_ERR_MISALIGNED, "found_nonfinite is not 4-byte aligned");
+  if ((st = check_aliasing(layer, Mode::kCheck, found_nonfinite, nullptr)) != LA_OK) return st;
+  la::Scalars s = {};
+  s.u = static_cast<float>(grad_unscale);
+  return enqueue(layer, Mode::kCheck, s, 0, total_numel(layer), found_nonfinite, nullptr,
+                 hip_stream);
+}
+
 LA_API int64_t la_state_bytes(const la_layer_desc* layer) {
   if (check_counts(layer) != LA_OK) return -1;
-  int64_t n = 0;
-  for (int i = 0; i < layer->num_tensors; ++i) n += layer->tensors[i].numel;
   // BF16/FP16 weights 2 + gradients 2 + FP32 master 4 + FP32 m and v 8
-  return 16 * n;
+  return 16 * total_numel(layer);
 }
 
 LA_API int64_t la_traffic_bytes(const la_layer_desc* layer) {
   if (check_counts(layer) != LA_OK) return -1;
-  int64_t n = 0;
-  for (int i = 0; i < layer->num_tensors; ++i) n += layer->tensors[i].numel;
-  // R gradient reads + master/m/v read and written + BF16 write
-  return (2 * static_cast<int64_t>(layer->num_replicas) + 26) * n;
+  // R gradient reads + master/m/v read and written + the compute copy
+  const int64_t out = layer->out_dtype == LA_OUT_NONE ? 0 : 2;
+  return (2 * static_cast<int64_t>(layer->num_replicas) + 24 + out) * total_numel(layer);
 }
 
 LA_API const char* la_last_error(void) { return g_error; }
 
-LA_API const char* la_version(void) { return "layeradam 0.1.0 gfx950"; }
+LA_API const char* la_version(void) { return "layeradam 0.2.0 gfx950"; }
 
 }  // extern "C"

@@ -8,6 +8,11 @@
 namespace la {
 
 constexpr int kMaxReplicas = 8;
+
+// Compute-copy formats (the values of la_out_dtype).
+constexpr int kOutBf16 = 0;
+constexpr int kOutFp16 = 1;
+constexpr int kOutNone = 2;
 // Tensors per kernel launch: their pointers travel in the kernel arguments
 // (about 104 bytes per tensor at R = 8).
 constexpr int kTensorsPerLaunch = 16;
@@ -43,9 +48,21 @@ struct LaunchShape {
 int target_workgroups_per_cu();
 
 // Enqueue the update of `count` (1..kTensorsPerLaunch) tensors in one launch.
+// flag: overflow flag or null; skip: device flag that makes the kernel a
+// no-op when non-zero, or null. A tensor entry with fewer than
+// chunk_elements() elements may have pointers aligned to their element size
+// only (it takes the element-wise path); larger entries need 16-byte
+// alignment of every pointer.
 hipError_t launch_layer_adam(const TensorArgs* tensors, int count, int replicas,
-                             bool fp16, const Scalars& s, int32_t* flag,
-                             hipStream_t stream, const LaunchShape& shape);
+                             bool fp16, int out_dtype, const Scalars& s, int32_t* flag,
+                             const int32_t* skip, hipStream_t stream,
+                             const LaunchShape& shape);
+
+// Enqueue the finite check of the aggregated gradients (sum of replicas times
+// unscale) of `count` tensors; sets *flag to 1 if one is +-Inf or NaN.
+hipError_t launch_check_gradients(const TensorArgs* tensors, int count, int replicas,
+                                  bool fp16, float unscale, int32_t* flag,
+                                  hipStream_t stream, const LaunchShape& shape);
 
 // Elements one workgroup processes per chunk.
 int64_t chunk_elements();

@@ -1,14 +1,19 @@
-// la_kernel.hip -- the fused LayerAdam kernel for gfx950.
+// la_kernel.hip -- the fused LayerAdam kernels for gfx950.
 //
-// One pass over HBM per layer: for every parameter it reads R gradient
-// replicas (2 bytes each) and the FP32 master, m and v (12 bytes), and
-// writes master, m, v (12 bytes) and the BF16 copy (2 bytes) -- (2R + 26)
-// bytes, the whole of the step's traffic. The arithmetic is the per-layer
-// mixed-precision Adam update that "SlideDP: Scaling Host-Resident LLM
-// Fine-Tuning Across Multiple GPUs" runs as its LayerAdam channel (sections
-// 核心方法 and 方法步骤详情) fused with the GPU-side reduction of the data-
-// parallel gradient that precedes it there; the BF16 cast is the FP32->BF16
-// conversion the SlideFormer page (technical summary 2.2) does on the host.
+// layer_adam_kernel: one pass over HBM per layer. For every parameter it
+// reads R gradient replicas (2 bytes each) and the FP32 master, m and v
+// (12 bytes), and writes master, m, v (12 bytes) and the 2-byte compute copy
+// -- (2R + 26) bytes, the whole of the step's traffic. The arithmetic is the
+// per-layer mixed-precision Adam update that "SlideDP: Scaling Host-Resident
+// LLM Fine-Tuning Across Multiple GPUs" runs as its LayerAdam channel
+// (sections 核心方法 and 方法步骤详情), fused with the GPU-side reduction of
+// the data-parallel gradient that precedes it there; the BF16 cast is the
+// FP32->BF16 conversion the SlideFormer page (technical summary 2.2) does on
+// the host, the FP16 cast the on-the-fly FP32->FP16 conversion of the
+// AutoHete page (section 2.2).
+//
+// check_kernel: the finite-check pre-pass of overflow-gated steps; reads the
+// R gradients only (2R bytes per parameter).
 //
 // Work decomposition. Every tensor of a launch is cut into chunks of
 // kChunk elements (the last chunk of a tensor may be partial); one launch
@@ -42,7 +47,8 @@ namespace la {
 namespace {
 
 // Tile shape and cache hints. The defaults are the measured best on MI355X
-// for the Qwen3-14B-shaped layer at R = 8; the macros exist so that other
+// for the Qwen3-14B-shaped layer at R = 8 (and within a few per cent of the
+// best on the other layer shapes measured); the macros exist so that other
 // shapes can be built and compared.
 #ifndef LA_BLOCK
 #define LA_BLOCK 128
@@ -62,12 +68,6 @@ namespace {
 #ifndef LA_WAVE_CONTIG
 #define LA_WAVE_CONTIG 1   // 1: each wave's tiles are adjacent in memory
 #endif
-#ifndef LA_STREAM_MAJOR
-#define LA_STREAM_MAJOR 0  // 1: issue all tiles of one stream before the next stream
-#endif
-#ifndef LA_STORE_MAJOR
-#define LA_STORE_MAJOR 0   // 1: compute every tile, then store stream by stream
-#endif
 #ifndef LA_WORKGROUPS_PER_CU
 #define LA_WORKGROUPS_PER_CU 2  // resident workgroups per compute unit (0: no cap)
 #endif
@@ -82,7 +82,7 @@ static_assert(kBlock % 64 == 0 && kBlock <= 1024, "whole waves");
 
 // Native vector types (the non-temporal builtins need them).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t grad_words __attribute__((ext_vector_type(kVec / 2)));  // kVec 16-bit values
+typedef uint32_t half_words __attribute__((ext_vector_type(kVec / 2)));  // kVec 16-bit values
 
 template <typename T>
 __device__ __forceinline__ T load_stream(const T* p) {
@@ -111,7 +111,8 @@ struct KernelArgs {
   KernelTensor<R> t[kTensorsPerLaunch];
   int64_t chunk_end[kTensorsPerLaunch];  // cumulative chunk counts
   Scalars s;
-  int32_t* flag;
+  int32_t* flag;         // overflow / found-non-finite flag, or null
+  const int32_t* skip;   // update only: skip everything if *skip != 0; or null
   int32_t count;
 };
 
@@ -144,14 +145,28 @@ __device__ __forceinline__ float decode_one(uint16_t bits) {
   }
 }
 
-// ---- FP32 -> BF16, round to nearest even ------------------------------------
-// Adding 0x7FFF plus the lowest kept bit carries into the kept half exactly
-// when the dropped half is above 0x8000, or equal to it with an odd kept half.
-// NaN is tested first and becomes the canonical quiet NaN 0x7FC0.
+// ---- FP32 -> compute copy ----------------------------------------------------
+// BF16, round to nearest even: adding 0x7FFF plus the lowest kept bit carries
+// into the kept half exactly when the dropped half is above 0x8000, or equal
+// to it with an odd kept half. NaN is tested first -> canonical 0x7FC0.
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
   const uint32_t b = __float_as_uint(x);
   const uint32_t rounded = (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
   return __builtin_isnan(x) ? 0x7FC0u : rounded;
+}
+
+// FP16: the hardware conversion rounds to nearest even (the default mode),
+// keeps binary16 subnormals (FP16 denormals are on) and overflows to Inf;
+// NaN -> canonical 0x7E00.
+__device__ __forceinline__ uint32_t fp16_bits(float x) {
+  const uint32_t h = __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+  return __builtin_isnan(x) ? 0x7E00u : h;
+}
+
+template <int OUT>
+__device__ __forceinline__ uint32_t out_bits(float x) {
+  if constexpr (OUT == kOutFp16) return fp16_bits(x);
+  else return bf16_bits(x);
 }
 
 // ---- one element of the update ----------------------------------------------
@@ -168,6 +183,26 @@ __device__ __forceinline__ Elem adam_update(float g, float p, float m, float v,
   return {p_new, m_new, v_new};
 }
 
+// Aggregated gradient of element k of a tile: left fold over the replicas in
+// replica order, then the unscale factor.
+template <int R, bool FP16>
+__device__ __forceinline__ float aggregate(const half_words (&G)[R], int k, float u) {
+  float g = (k & 1) ? decode_hi<FP16>(G[0][k / 2]) : decode_lo<FP16>(G[0][k / 2]);
+#pragma unroll
+  for (int r = 1; r < R; ++r)
+    g = g + ((k & 1) ? decode_hi<FP16>(G[r][k / 2]) : decode_lo<FP16>(G[r][k / 2]));
+  return g * u;
+}
+
+template <int R, bool FP16>
+__device__ __forceinline__ float aggregate_one(const uint16_t* const (&g)[R], int64_t i,
+                                               float u) {
+  float x = decode_one<FP16>(g[0][i]);
+#pragma unroll
+  for (int r = 1; r < R; ++r) x = x + decode_one<FP16>(g[r][i]);
+  return x * u;
+}
+
 // Element offset, within its chunk, of thread tid's first element in tile u.
 // Tile-major: tile u covers [u * kBlock * kVec, (u + 1) * kBlock * kVec).
 // Wave-contiguous: wave w owns kUnroll adjacent runs of 64 * kVec elements.
@@ -179,7 +214,9 @@ __device__ __forceinline__ uint32_t tile_offset(int u, int tid) {
   }
 }
 
-// Store one tile's results: master, m, v as 16-byte vectors, BF16 packed.
+// Store one tile's results: master, m, v as 16-byte vectors, the compute
+// copy packed two values per 32-bit word.
+template <int OUT>
 __device__ __forceinline__ void store_tile(const Elem* e, float* p, float* m, float* v,
                                            uint16_t* w, uint32_t off) {
 #pragma unroll
@@ -189,16 +226,31 @@ __device__ __forceinline__ void store_tile(const Elem* e, float* p, float* m, fl
     store_stream(f32x4{x[0].m, x[1].m, x[2].m, x[3].m}, reinterpret_cast<f32x4*>(m + off) + q);
     store_stream(f32x4{x[0].v, x[1].v, x[2].v, x[3].v}, reinterpret_cast<f32x4*>(v + off) + q);
   }
-  grad_words wb;
+  if constexpr (OUT != kOutNone) {
+    half_words wb;
 #pragma unroll
-  for (int k = 0; k < kVec; k += 2) wb[k / 2] = bf16_bits(e[k].p) | (bf16_bits(e[k + 1].p) << 16);
-  store_stream(wb, reinterpret_cast<grad_words*>(w + off));
+    for (int k = 0; k < kVec; k += 2)
+      wb[k / 2] = out_bits<OUT>(e[k].p) | (out_bits<OUT>(e[k + 1].p) << 16);
+    store_stream(wb, reinterpret_cast<half_words*>(w + off));
+  }
 }
 
-// ---- the kernel ---------------------------------------------------------------
-template <int R, bool FP16, bool FLAG>
+// Tensor of chunk c. Chunks only move forward within a workgroup, so t and
+// first_chunk_of_t carry over between iterations.
+template <int R>
+__device__ __forceinline__ void locate(const KernelArgs<R>& a, int64_t c, int& t,
+                                       int64_t& first_chunk_of_t) {
+  while (c >= a.chunk_end[t]) {  // uniform across the workgroup
+    first_chunk_of_t = a.chunk_end[t];
+    ++t;
+  }
+}
+
+// ---- the update kernel ---------------------------------------------------------
+template <int R, bool FP16, bool FLAG, int OUT>
 __global__ void __launch_bounds__(kBlock)
 layer_adam_kernel(const KernelArgs<R> a) {
+  if (a.skip != nullptr && *a.skip != 0) return;  // gated step: overflowed, skip
   const int tid = threadIdx.x;
   const int64_t total_chunks = a.chunk_end[a.count - 1];
   const Scalars s = a.s;
@@ -207,10 +259,7 @@ layer_adam_kernel(const KernelArgs<R> a) {
   int t = 0;
   int64_t first_chunk_of_t = 0;
   for (int64_t c = blockIdx.x; c < total_chunks; c += gridDim.x) {
-    while (c >= a.chunk_end[t]) {  // uniform: chunks only move forward
-      first_chunk_of_t = a.chunk_end[t];
-      ++t;
-    }
+    locate(a, c, t, first_chunk_of_t);
     const KernelTensor<R>& T = a.t[t];
     const int64_t base = (c - first_chunk_of_t) * kChunk;
     const int64_t n = T.numel;
@@ -218,7 +267,7 @@ layer_adam_kernel(const KernelArgs<R> a) {
     float* __restrict__ p = T.p + base;
     float* __restrict__ m = T.m + base;
     float* __restrict__ v = T.v + base;
-    uint16_t* __restrict__ w = T.w + base;
+    uint16_t* __restrict__ w = OUT == kOutNone ? nullptr : T.w + base;
     const uint16_t* g[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) g[r] = T.g[r] + base;
@@ -226,92 +275,30 @@ layer_adam_kernel(const KernelArgs<R> a) {
     if (base + kChunk <= n) {
       // Full chunk: vector loads of every tile first, then the arithmetic.
       f32x4 P[kUnroll][kQuads], M[kUnroll][kQuads], V[kUnroll][kQuads];
-      grad_words G[kUnroll][R];
-      if constexpr (LA_STREAM_MAJOR) {
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-          for (int u = 0; u < kUnroll; ++u)
-            G[u][r] = load_stream(reinterpret_cast<const grad_words*>(g[r] + tile_offset(u, tid)));
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-          for (int q = 0; q < kQuads; ++q)
-            P[u][q] = load_stream(reinterpret_cast<const f32x4*>(p + tile_offset(u, tid)) + q);
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-          for (int q = 0; q < kQuads; ++q)
-            M[u][q] = load_stream(reinterpret_cast<const f32x4*>(m + tile_offset(u, tid)) + q);
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-          for (int q = 0; q < kQuads; ++q)
-            V[u][q] = load_stream(reinterpret_cast<const f32x4*>(v + tile_offset(u, tid)) + q);
-      } else {
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          const uint32_t off = tile_offset(u, tid);
-#pragma unroll
-          for (int q = 0; q < kQuads; ++q) {
-            P[u][q] = load_stream(reinterpret_cast<const f32x4*>(p + off) + q);
-            M[u][q] = load_stream(reinterpret_cast<const f32x4*>(m + off) + q);
-            V[u][q] = load_stream(reinterpret_cast<const f32x4*>(v + off) + q);
-          }
-#pragma unroll
-          for (int r = 0; r < R; ++r)
-            G[u][r] = load_stream(reinterpret_cast<const grad_words*>(g[r] + off));
-        }
-      }
-      Elem e[kUnroll][kVec];
+      half_words G[kUnroll][R];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
+        const uint32_t off = tile_offset(u, tid);
+#pragma unroll
+        for (int q = 0; q < kQuads; ++q) {
+          P[u][q] = load_stream(reinterpret_cast<const f32x4*>(p + off) + q);
+          M[u][q] = load_stream(reinterpret_cast<const f32x4*>(m + off) + q);
+          V[u][q] = load_stream(reinterpret_cast<const f32x4*>(v + off) + q);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          G[u][r] = load_stream(reinterpret_cast<const half_words*>(g[r] + off));
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        Elem e[kVec];
 #pragma unroll
         for (int k = 0; k < kVec; ++k) {
-          // left fold over the replicas, in replica order
-          float gk = (k & 1) ? decode_hi<FP16>(G[u][0][k / 2]) : decode_lo<FP16>(G[u][0][k / 2]);
-#pragma unroll
-          for (int r = 1; r < R; ++r)
-            gk = gk + ((k & 1) ? decode_hi<FP16>(G[u][r][k / 2]) : decode_lo<FP16>(G[u][r][k / 2]));
-          gk = gk * s.u;
+          const float gk = aggregate<R, FP16>(G[u], k, s.u);
           if (FLAG) bad |= !__builtin_isfinite(gk);
-          e[u][k] = adam_update(gk, P[u][k / 4][k % 4], M[u][k / 4][k % 4], V[u][k / 4][k % 4], s);
+          e[k] = adam_update(gk, P[u][k / 4][k % 4], M[u][k / 4][k % 4], V[u][k / 4][k % 4], s);
         }
-        if constexpr (!LA_STORE_MAJOR) store_tile(e[u], p, m, v, w, tile_offset(u, tid));
-      }
-      if constexpr (LA_STORE_MAJOR) {
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-          for (int q = 0; q < kQuads; ++q) {
-            const Elem* x = e[u] + 4 * q;
-            store_stream(f32x4{x[0].p, x[1].p, x[2].p, x[3].p},
-                         reinterpret_cast<f32x4*>(p + tile_offset(u, tid)) + q);
-          }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-          for (int q = 0; q < kQuads; ++q) {
-            const Elem* x = e[u] + 4 * q;
-            store_stream(f32x4{x[0].m, x[1].m, x[2].m, x[3].m},
-                         reinterpret_cast<f32x4*>(m + tile_offset(u, tid)) + q);
-          }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-          for (int q = 0; q < kQuads; ++q) {
-            const Elem* x = e[u] + 4 * q;
-            store_stream(f32x4{x[0].v, x[1].v, x[2].v, x[3].v},
-                         reinterpret_cast<f32x4*>(v + tile_offset(u, tid)) + q);
-          }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          grad_words wb;
-#pragma unroll
-          for (int k = 0; k < kVec; k += 2)
-            wb[k / 2] = bf16_bits(e[u][k].p) | (bf16_bits(e[u][k + 1].p) << 16);
-          store_stream(wb, reinterpret_cast<grad_words*>(w + tile_offset(u, tid)));
-        }
+        store_tile<OUT>(e, p, m, v, w, tile_offset(u, tid));
       }
     } else {
       // Last, partial chunk of a tensor: element by element, bounds-checked.
@@ -322,16 +309,13 @@ layer_adam_kernel(const KernelArgs<R> a) {
         for (int k = 0; k < kVec; ++k) {
           const int64_t i = static_cast<int64_t>((u * kBlock + tid) * kVec + k);
           if (i < left) {
-            float gk = decode_one<FP16>(g[0][i]);
-#pragma unroll
-            for (int r = 1; r < R; ++r) gk = gk + decode_one<FP16>(g[r][i]);
-            gk = gk * s.u;
+            const float gk = aggregate_one<R, FP16>(g, i, s.u);
             if (FLAG) bad |= !__builtin_isfinite(gk);
             const Elem e = adam_update(gk, p[i], m[i], v[i], s);
             p[i] = e.p;
             m[i] = e.m;
             v[i] = e.v;
-            w[i] = static_cast<uint16_t>(bf16_bits(e.p));
+            if constexpr (OUT != kOutNone) w[i] = static_cast<uint16_t>(out_bits<OUT>(e.p));
           }
         }
       }
@@ -344,10 +328,59 @@ layer_adam_kernel(const KernelArgs<R> a) {
   }
 }
 
-template <int R, bool FP16, bool FLAG>
-hipError_t launch_typed(const TensorArgs* ts, int count, const Scalars& s,
-                        int32_t* flag, hipStream_t stream, const LaunchShape& shape) {
-  KernelArgs<R> a = {};
+// ---- the finite-check pre-pass -------------------------------------------------
+template <int R, bool FP16>
+__global__ void __launch_bounds__(kBlock)
+check_kernel(const KernelArgs<R> a) {
+  if (*a.flag != 0) return;  // already found: the answer cannot change
+  const int tid = threadIdx.x;
+  const int64_t total_chunks = a.chunk_end[a.count - 1];
+  const float u = a.s.u;
+  bool bad = false;
+
+  int t = 0;
+  int64_t first_chunk_of_t = 0;
+  for (int64_t c = blockIdx.x; c < total_chunks; c += gridDim.x) {
+    locate(a, c, t, first_chunk_of_t);
+    const KernelTensor<R>& T = a.t[t];
+    const int64_t base = (c - first_chunk_of_t) * kChunk;
+    const int64_t n = T.numel;
+    const uint16_t* g[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) g[r] = T.g[r] + base;
+
+    if (base + kChunk <= n) {
+      half_words G[kUnroll][R];
+#pragma unroll
+      for (int tile = 0; tile < kUnroll; ++tile) {
+        const uint32_t off = tile_offset(tile, tid);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          G[tile][r] = load_stream(reinterpret_cast<const half_words*>(g[r] + off));
+      }
+#pragma unroll
+      for (int tile = 0; tile < kUnroll; ++tile)
+#pragma unroll
+        for (int k = 0; k < kVec; ++k)
+          bad |= !__builtin_isfinite(aggregate<R, FP16>(G[tile], k, u));
+    } else {
+      const int64_t left = n - base;
+#pragma unroll 1
+      for (int tile = 0; tile < kUnroll; ++tile) {
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) {
+          const int64_t i = static_cast<int64_t>((tile * kBlock + tid) * kVec + k);
+          if (i < left) bad |= !__builtin_isfinite(aggregate_one<R, FP16>(g, i, u));
+        }
+      }
+    }
+  }
+  if (__any(bad) && __lane_id() == 0) atomicOr(a.flag, 1);
+}
+
+// ---- launch --------------------------------------------------------------------
+template <int R>
+int64_t fill_args(KernelArgs<R>& a, const TensorArgs* ts, int count) {
   int64_t chunks = 0;
   for (int i = 0; i < count; ++i) {
     a.t[i].p = ts[i].p;
@@ -359,24 +392,69 @@ hipError_t launch_typed(const TensorArgs* ts, int count, const Scalars& s,
     chunks += (ts[i].numel + kChunk - 1) / kChunk;
     a.chunk_end[i] = chunks;
   }
+  a.count = count;
+  return chunks;
+}
+
+hipError_t launch(const void* kernel, void* args, int64_t chunks, hipStream_t stream,
+                  const LaunchShape& shape) {
+  const int64_t grid = chunks < shape.grid_cap ? chunks : shape.grid_cap;  // >= 1
+  void* params[] = {args};
+  return hipLaunchKernel(kernel, dim3(static_cast<unsigned>(grid)), dim3(kBlock), params,
+                         static_cast<unsigned>(shape.lds_bytes), stream);
+}
+
+template <int R, bool FP16, bool FLAG, int OUT>
+hipError_t launch_update_typed(const TensorArgs* ts, int count, const Scalars& s,
+                               int32_t* flag, const int32_t* skip, hipStream_t stream,
+                               const LaunchShape& shape) {
+  KernelArgs<R> a = {};
+  const int64_t chunks = fill_args(a, ts, count);
   a.s = s;
   a.flag = flag;
-  a.count = count;
-  const int64_t grid = chunks < shape.grid_cap ? chunks : shape.grid_cap;  // >= 1
-  void* args[] = {&a};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&layer_adam_kernel<R, FP16, FLAG>),
-                         dim3(static_cast<unsigned>(grid)), dim3(kBlock), args, static_cast<unsigned>(shape.lds_bytes), stream);
+  a.skip = skip;
+  return launch(reinterpret_cast<const void*>(&layer_adam_kernel<R, FP16, FLAG, OUT>), &a,
+                chunks, stream, shape);
+}
+
+template <int R, bool FP16, int OUT>
+hipError_t launch_update_flag(const TensorArgs* ts, int count, const Scalars& s,
+                              int32_t* flag, const int32_t* skip, hipStream_t stream,
+                              const LaunchShape& shape) {
+  return flag ? launch_update_typed<R, FP16, true, OUT>(ts, count, s, flag, skip, stream, shape)
+              : launch_update_typed<R, FP16, false, OUT>(ts, count, s, flag, skip, stream, shape);
+}
+
+template <int R, bool FP16>
+hipError_t launch_update_out(const TensorArgs* ts, int count, int out, const Scalars& s,
+                             int32_t* flag, const int32_t* skip, hipStream_t stream,
+                             const LaunchShape& shape) {
+  switch (out) {
+    case kOutBf16: return launch_update_flag<R, FP16, kOutBf16>(ts, count, s, flag, skip, stream, shape);
+    case kOutFp16: return launch_update_flag<R, FP16, kOutFp16>(ts, count, s, flag, skip, stream, shape);
+    case kOutNone: return launch_update_flag<R, FP16, kOutNone>(ts, count, s, flag, skip, stream, shape);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int R>
-hipError_t launch_r(const TensorArgs* ts, int count, bool fp16, const Scalars& s,
-                    int32_t* flag, hipStream_t stream, const LaunchShape& shape) {
-  if (fp16) {
-    return flag ? launch_typed<R, true, true>(ts, count, s, flag, stream, shape)
-                : launch_typed<R, true, false>(ts, count, s, flag, stream, shape);
-  }
-  return flag ? launch_typed<R, false, true>(ts, count, s, flag, stream, shape)
-              : launch_typed<R, false, false>(ts, count, s, flag, stream, shape);
+hipError_t launch_update_r(const TensorArgs* ts, int count, bool fp16, int out,
+                           const Scalars& s, int32_t* flag, const int32_t* skip,
+                           hipStream_t stream, const LaunchShape& shape) {
+  return fp16 ? launch_update_out<R, true>(ts, count, out, s, flag, skip, stream, shape)
+              : launch_update_out<R, false>(ts, count, out, s, flag, skip, stream, shape);
+}
+
+template <int R>
+hipError_t launch_check_r(const TensorArgs* ts, int count, bool fp16, float u, int32_t* flag,
+                          hipStream_t stream, const LaunchShape& shape) {
+  KernelArgs<R> a = {};
+  const int64_t chunks = fill_args(a, ts, count);
+  a.s.u = u;
+  a.flag = flag;
+  const void* k = fp16 ? reinterpret_cast<const void*>(&check_kernel<R, true>)
+                       : reinterpret_cast<const void*>(&check_kernel<R, false>);
+  return launch(k, &a, chunks, stream, shape);
 }
 
 }  // namespace
@@ -385,18 +463,29 @@ int64_t chunk_elements() { return kChunk; }
 
 int target_workgroups_per_cu() { return LA_WORKGROUPS_PER_CU; }
 
-hipError_t launch_layer_adam(const TensorArgs* tensors, int count, int replicas,
-                             bool fp16, const Scalars& s, int32_t* flag,
-                             hipStream_t stream, const LaunchShape& shape) {
+hipError_t launch_layer_adam(const TensorArgs* tensors, int count, int replicas, bool fp16,
+                             int out_dtype, const Scalars& s, int32_t* flag,
+                             const int32_t* skip, hipStream_t stream,
+                             const LaunchShape& shape) {
   switch (replicas) {
-    case 1: return launch_r<1>(tensors, count, fp16, s, flag, stream, shape);
-    case 2: return launch_r<2>(tensors, count, fp16, s, flag, stream, shape);
-    case 3: return launch_r<3>(tensors, count, fp16, s, flag, stream, shape);
-    case 4: return launch_r<4>(tensors, count, fp16, s, flag, stream, shape);
-    case 5: return launch_r<5>(tensors, count, fp16, s, flag, stream, shape);
-    case 6: return launch_r<6>(tensors, count, fp16, s, flag, stream, shape);
-    case 7: return launch_r<7>(tensors, count, fp16, s, flag, stream, shape);
-    case 8: return launch_r<8>(tensors, count, fp16, s, flag, stream, shape);
+#define LA_CASE(RR)                                                                      \
+  case RR:                                                                               \
+    return launch_update_r<RR>(tensors, count, fp16, out_dtype, s, flag, skip, stream, \
+                               shape);
+    LA_CASE(1) LA_CASE(2) LA_CASE(3) LA_CASE(4) LA_CASE(5) LA_CASE(6) LA_CASE(7) LA_CASE(8)
+#undef LA_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_check_gradients(const TensorArgs* tensors, int count, int replicas,
+                                  bool fp16, float unscale, int32_t* flag, hipStream_t stream,
+                                  const LaunchShape& shape) {
+  switch (replicas) {
+#define LA_CASE(RR) \
+  case RR: return launch_check_r<RR>(tensors, count, fp16, unscale, flag, stream, shape);
+    LA_CASE(1) LA_CASE(2) LA_CASE(3) LA_CASE(4) LA_CASE(5) LA_CASE(6) LA_CASE(7) LA_CASE(8)
+#undef LA_CASE
     default: return hipErrorInvalidValue;
   }
 }

@@ -54,18 +54,23 @@ class GpuLayer:
     lays them out: one allocation per master/m/v/BF16 tensor, one flat
     buffer per gradient replica with tensor views at multiples of 8."""
 
-    def __init__(self, L: synth.LayerInputs, device="cuda:0"):
+    def __init__(self, L: synth.LayerInputs, device="cuda:0", out: str = "bf16"):
         self.L = L
+        self.out = out
         w = L.workload
         dev = torch.device(device)
         gdt = grad_torch_dtype(w)
         self.params = []
+        self.out_buffers = []
+        odt = {"bf16": torch.bfloat16, "fp16": torch.float16, "none": torch.bfloat16}[out]
         for i, (_, n) in enumerate(w.tensors):
             p = torch.from_numpy(L.master[i]).to(dev)
             m = torch.from_numpy(L.exp_avg[i]).to(dev)
             v = torch.from_numpy(L.exp_avg_sq[i]).to(dev)
-            wb = torch.full((n,), 0x7FAA, dtype=torch.int16, device=dev).view(torch.bfloat16)
-            self.params.append((p, m, v, wb))
+            # 0x7FAA: a NaN payload neither cast produces, to spot unwritten elements
+            wb = torch.full((n,), 0x7FAA, dtype=torch.int16, device=dev).view(odt)
+            self.out_buffers.append(wb)
+            self.params.append((p, m, v, None if out == "none" else wb))
         self.grad_flat = [to_device_u16(g, gdt, dev) for g in L.grad_flat]
         self.grads = [[gf[off:off + n] for gf in self.grad_flat]
                       for off, (_, n) in zip(L.grad_offsets, w.tensors)]
@@ -83,7 +88,7 @@ class GpuLayer:
     def download(self) -> Dict[str, List[np.ndarray]]:
         torch.cuda.synchronize()
         out = {"master": [], "exp_avg": [], "exp_avg_sq": [], "weight_out": []}
-        for p, m, v, wb in self.params:
+        for (p, m, v, _), wb in zip(self.params, self.out_buffers):
             out["master"].append(p.cpu().numpy())
             out["exp_avg"].append(m.cpu().numpy())
             out["exp_avg_sq"].append(v.cpu().numpy())
@@ -92,7 +97,7 @@ class GpuLayer:
         return out
 
     def free(self):
-        self.params = self.grads = self.grad_flat = None
+        self.params = self.grads = self.grad_flat = self.out_buffers = None
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
 
@@ -111,14 +116,15 @@ def oracle_tensors(L: synth.LayerInputs, idx: Optional[Sequence[np.ndarray]] = N
 
 
 def oracle_step(L: synth.LayerInputs, ts, t: Optional[int] = None,
-                with_flag: Optional[bool] = None, **hp_over) -> Optional[int]:
+                with_flag: Optional[bool] = None, out: str = "bf16",
+                **hp_over) -> Optional[int]:
     w = L.workload
     hp = dict(w.hyper)
     hp.update(hp_over)
     unscale = hp.pop("unscale", w.unscale)
     use_flag = w.with_flag if with_flag is None else with_flag
     return oracle.step(ts, dtype=w.grad_dtype, step=w.step if t is None else t,
-                       unscale=unscale, with_flag=use_flag, **hp)
+                       unscale=unscale, with_flag=use_flag, out_dtype=out, **hp)
 
 
 @dataclass
@@ -134,9 +140,11 @@ class Report:
 
 
 def compare(gpu: Dict[str, List[np.ndarray]], ts, idx=None, report: Optional[Report] = None,
-            label: str = "") -> Report:
+            label: str = "", out: str = "bf16") -> Report:
     """Compare GPU outputs (whole tensors, or sampled at idx) with oracle
-    tensors; assert the parity bar and return statistics."""
+    tensors; assert the parity bar and return statistics. ``out`` is the
+    compute-copy format ("bf16", "fp16", or "none": the buffer must still hold
+    its 0x7FAA fill)."""
     rep = report or Report()
     for i, x in enumerate(ts):
         sel = slice(None) if idx is None else idx[i]
@@ -152,17 +160,22 @@ def compare(gpu: Dict[str, List[np.ndarray]], ts, idx=None, report: Optional[Rep
             rep.max_ulp = max(rep.max_ulp, worst)
             rep.nonzero_ulp += int(np.count_nonzero(d))
         gw = gpu["weight_out"][i][sel]
-        # the BF16 copy is exactly the RNE cast of the GPU's own master ...
-        own = oracle.round_bf16(gpu["master"][i][sel])
+        if out == "none":
+            assert np.all(gw == 0x7FAA), f"{label} tensor {i}: compute copy written"
+            rep.compared += int(gw.size)
+            continue
+        # the compute copy is exactly the RNE cast of the GPU's own master ...
+        cast = oracle.round_fp16 if out == "fp16" else oracle.round_bf16
+        own = cast(gpu["master"][i][sel])
         bad = np.nonzero(gw != own)[0]
         if bad.size:
             j = int(bad[0])
             raise AssertionError(f"{label} tensor {i} weight_out[{j}] = {gw[j]:#06x}, "
-                                 f"RNE(master) = {own[j]:#06x}")
+                                 f"RNE_{out}(master) = {own[j]:#06x}")
         # ... and equals the oracle's wherever the masters agree bit for bit
         same = gpu["master"][i][sel].view(np.uint32) == x.master.view(np.uint32)
         rep.bf16_mismatch += int(np.count_nonzero((gw != x.weight_out) & same))
-        assert rep.bf16_mismatch == 0, f"{label} tensor {i}: BF16 differs where masters agree"
+        assert rep.bf16_mismatch == 0, f"{label} tensor {i}: copy differs where masters agree"
         rep.compared += int(gw.size)
     return rep
 

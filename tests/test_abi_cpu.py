@@ -93,6 +93,11 @@ def test_workload_sizes():
         assert synth.WORKLOADS[name].numel == n
 
 
+def test_traffic_without_a_compute_copy():
+    assert la.traffic_bytes([1000, 24], 8, la.OUT_NONE) == (2 * 8 + 24) * 1024
+    assert la.traffic_bytes([1000, 24], 8, la.OUT_FP16) == (2 * 8 + 26) * 1024
+
+
 def test_accounting_rejects_bad_descriptors():
     desc, keep = la.make_layer([dict(numel=10)], 0, la.GRAD_BF16)
     assert la.state_bytes_raw(desc) == -1
@@ -192,6 +197,77 @@ def test_overlapping_buffers(case):
     elif case == "flag_in_master":
         flag = a["master"] + 64
     expect_status([a, b], 2, la.GRAD_BF16, HP, 3, flag=flag)
+
+
+@host_only
+def test_unknown_output_format():
+    desc, keep = la.make_layer([fake_tensor(0)], 2, la.GRAD_BF16, 3)
+    with pytest.raises(la.LayerAdamError) as e:
+        la.step_raw(desc, la.make_params(**HP))
+    assert e.value.status == 4
+
+
+@host_only
+@pytest.mark.parametrize("rng_", [(-1, 10), (5, 4), (0, 2049), (2049, 2049)])
+def test_element_range_outside_the_layer(rng_):
+    desc, keep = la.make_layer([fake_tensor(0, n=1024), fake_tensor(1, n=1024)], 2,
+                               la.GRAD_BF16)
+    with pytest.raises(la.LayerAdamError) as e:
+        la.step_range_raw(desc, la.make_params(**HP), *rng_)
+    assert e.value.status == 1
+
+
+@host_only
+@pytest.mark.parametrize("case", ["null", "misaligned", "on_master", "on_weight"])
+def test_bad_skip_flag(case):
+    t = fake_tensor(0)
+    skip = {"null": 0, "misaligned": BASE + 0x50000002, "on_master": t["master"] + 128,
+            "on_weight": t["weight_out"]}[case]
+    desc, keep = la.make_layer([t], 2, la.GRAD_BF16)
+    with pytest.raises(la.LayerAdamError) as e:
+        la.step_gated_raw(desc, la.make_params(**HP), skip)
+    assert e.value.status == {"null": 1, "misaligned": 2, "on_master": 3, "on_weight": 3}[case]
+
+
+@host_only
+@pytest.mark.parametrize("case", ["null", "misaligned", "on_grad", "unscale0", "null_grad"])
+def test_bad_gradient_check(case):
+    t = fake_tensor(0)
+    flag, unscale = BASE + 0x50000000, 1.0
+    if case == "null":
+        flag = 0
+    elif case == "misaligned":
+        flag += 2
+    elif case == "on_grad":
+        flag = t["grads"][1] + 64
+    elif case == "unscale0":
+        unscale = 0.0
+    elif case == "null_grad":
+        t["grads"][0] = 0
+    desc, keep = la.make_layer([t], 2, la.GRAD_BF16)
+    with pytest.raises(la.LayerAdamError) as e:
+        la.check_gradients_raw(desc, unscale, flag)
+    assert e.value.status == {"null": 1, "misaligned": 2, "on_grad": 3, "unscale0": 1,
+                              "null_grad": 1}[case]
+
+
+@host_only
+def test_buffers_a_mode_does_not_touch_are_not_required():
+    # the gradient check reads gradients only; without a compute copy the
+    # output pointer is ignored. Both pass validation and reach the (absent)
+    # device here.
+    t = fake_tensor(0)
+    t.update(master=0, exp_avg=0, exp_avg_sq=0, weight_out=0)
+    desc, keep = la.make_layer([t], 2, la.GRAD_BF16)
+    with pytest.raises(la.LayerAdamError) as e:
+        la.check_gradients_raw(desc, 1.0, BASE + 0x50000000)
+    assert e.value.status == 5
+    t = fake_tensor(0)
+    t["weight_out"] = 0
+    desc, keep = la.make_layer([t], 2, la.GRAD_BF16, la.OUT_NONE)
+    with pytest.raises(la.LayerAdamError) as e:
+        la.step_raw(desc, la.make_params(**HP))
+    assert e.value.status == 5
 
 
 @host_only

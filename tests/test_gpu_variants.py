@@ -1,0 +1,237 @@
+"""The other entry points and output formats, against the oracle, on MI355X:
+FP16 and no compute copy, element-range updates, the gradient finite check
+and the overflow-gated step."""
+import numpy as np
+import pytest
+import torch
+
+import optimizer_step_layeradam_amd as la
+import oracle
+import synth
+from lahelpers import GpuLayer, compare, log, oracle_step, oracle_tensors
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = (("a", 1), ("b", 3), ("c", 7), ("d", 2047), ("e", 2048), ("f", 2049),
+          ("g", 4101), ("h", 10001), ("i", 65536 + 13))
+
+
+def ragged(R, dtype="bf16", seed=3000, **kw):
+    return synth.Workload(name=f"ragged_R{R}_{dtype}", seed=seed + R, tensors=RAGGED,
+                          replicas=R, grad_dtype=dtype, step=5, **kw)
+
+
+# ---------------------------------------------------------------------------
+# Compute-copy formats
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("out", ["fp16", "none"])
+@pytest.mark.parametrize("R", [1, 4, 8])
+def test_compute_copy_format(R, out):
+    w = ragged(R)
+    log(f"case out={out} R={R}")
+    L = synth.make_layer(w)
+    gl = GpuLayer(L, out=out)
+    gl.step()
+    ts = oracle_tensors(L)
+    oracle_step(L, ts, out=out)
+    log(f"  {compare(gl.download(), ts, label=w.name, out=out)}")
+    gl.free()
+
+
+@pytest.mark.parametrize("out", ["bf16", "fp16"])
+def test_cast_of_every_rounding_case(out):
+    """lr = 0, zero gradients and moments: the new master equals the old bit
+    for bit, so the compute copy is the cast of chosen FP32 patterns: every
+    exponent and sign with the rounding-relevant low bits, plus Inf and NaN."""
+    highs = np.arange(65536, dtype=np.uint32) << 16
+    lows = np.array([0x0000, 0x0001, 0x0FFF, 0x1000, 0x1001, 0x1FFF, 0x2000, 0x3FFF, 0x4000,
+                     0x7FFF, 0x8000, 0x8001, 0xBFFF, 0xC000, 0xEFFF, 0xF000, 0xFFFF],
+                    dtype=np.uint32)
+    pats = (highs[:, None] | lows[None, :]).ravel()
+    n = pats.size
+    log(f"case cast {out}: {n} patterns")
+    w = synth.Workload(name=f"cast_{out}", seed=3100, tensors=(("x", n),), replicas=1,
+                       grad_dtype="bf16", step=1, m_std=None, v_high=None)
+    L = synth.make_layer(w)
+    L.master[0][:] = pats.view(np.float32)
+    L.grad_flat[0][:] = 0
+    gl = GpuLayer(L, out=out)
+    gl.step(lr=0.0)
+    got = gl.download()
+    gl.free()
+    x = got["master"][0]
+    num = ~np.isnan(pats.view(np.float32))              # p * 1 - 0 quiets a NaN
+    assert np.array_equal(x.view(np.uint32)[num], pats[num])   # master unchanged
+    assert np.all(np.isnan(x[~num]))
+    cast = oracle.round_fp16 if out == "fp16" else oracle.round_bf16
+    want = cast(pats.view(np.float32))
+    bad = np.nonzero(got["weight_out"][0] != want)[0]
+    assert bad.size == 0, (f"{bad.size} mismatches, first pattern {hex(int(pats[bad[0]]))}: "
+                           f"gpu {got['weight_out'][0][bad[0]]:#06x} oracle {want[bad[0]]:#06x}")
+
+
+# ---------------------------------------------------------------------------
+# Element ranges
+# ---------------------------------------------------------------------------
+def _partition(n, rng, pieces):
+    cuts = np.sort(rng.integers(0, n + 1, pieces - 1))
+    bounds = np.concatenate([[0], cuts, [n]])
+    return list(zip(bounds[:-1].tolist(), bounds[1:].tolist()))
+
+
+@pytest.mark.parametrize("pieces", [1, 2, 7, 40])
+def test_ranges_over_a_partition_equal_one_whole_step(pieces):
+    w = ragged(3, with_flag=True)
+    log(f"case ranges pieces={pieces}")
+    L = synth.make_layer(w)
+    gl = GpuLayer(L)
+    rng = np.random.default_rng(pieces)
+    parts = _partition(w.numel, rng, pieces)
+    # include ranges that end exactly at tensor boundaries and empty ones
+    for lo, hi in reversed(parts):
+        la.step_range(gl.params, gl.grads, lo, hi, step=w.step, overflow_flag=gl.flag,
+                      **w.hyper)
+        la.step_range(gl.params, gl.grads, hi, hi, step=w.step, **w.hyper)  # empty: no-op
+    ts = oracle_tensors(L)
+    flag = oracle_step(L, ts)
+    got = gl.download()
+    rep = compare(got, ts, label=f"ranges{pieces}")
+    assert rep.max_ulp == 0 and got["flag"] == flag == 0
+    gl.free()
+
+
+def test_fixed_size_chunks_over_a_layer():
+    """The layer released in fixed-size chunks, as a producer would hand over
+    reduced gradients chunk by chunk, on a side stream that waits on an
+    event per chunk."""
+    w = synth.shrink(synth.WORKLOADS["qwen3_4b_layer"], 16)
+    log(f"case chunks N={w.numel}")
+    L = synth.make_layer(w)
+    gl = GpuLayer(L)
+    chunk = 1_000_003
+    side = torch.cuda.Stream()
+    for lo in range(0, w.numel, chunk):
+        ready = torch.cuda.Event()
+        ready.record(torch.cuda.current_stream())
+        side.wait_event(ready)
+        la.step_range(gl.params, gl.grads, lo, min(w.numel, lo + chunk), step=w.step,
+                      stream=side, **w.hyper)
+    side.synchronize()
+    ts = oracle_tensors(L)
+    oracle_step(L, ts)
+    log(f"  {compare(gl.download(), ts, label='chunks')}")
+    gl.free()
+
+
+def test_range_with_fp16_gradients_and_copy():
+    w = ragged(2, "fp16", grad_prescale=1024.0, unscale=1 / 1024)
+    L = synth.make_layer(w)
+    gl = GpuLayer(L, out="fp16")
+    for lo, hi in _partition(w.numel, np.random.default_rng(9), 13):
+        la.step_range(gl.params, gl.grads, lo, hi, step=w.step, grad_unscale=w.unscale,
+                      **w.hyper)
+    ts = oracle_tensors(L)
+    oracle_step(L, ts, out="fp16")
+    compare(gl.download(), ts, label="range_fp16", out="fp16")
+    gl.free()
+
+
+# ---------------------------------------------------------------------------
+# Gradient check and gated step
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("inject", [None, "inf", "nan", "cancel", "unscale"])
+def test_gradient_check_matches_the_oracle(dtype, inject):
+    w = ragged(4, dtype)
+    log(f"case check {dtype} {inject}")
+    L = synth.make_layer(w)
+    unscale = 1.0
+    codes = {"bf16": (0x7F80, 0xFF80, 0x7FC1, 0x7F7F), "fp16": (0x7C00, 0xFC00, 0x7E01, 0x7BFF)}
+    inf, ninf, nan, big = codes[dtype]
+    if inject == "inf":
+        L.grad(2, 8)[65536 + 12] = inf        # last element of the last tensor
+    elif inject == "nan":
+        L.grad(0, 3)[1000] = nan
+    elif inject == "cancel":
+        L.grad(1, 5)[7], L.grad(3, 5)[7] = inf, ninf
+    elif inject == "unscale":
+        for r in range(4):
+            L.grad(r, 6)[5] = big
+        unscale = 2.0 ** 112 if dtype == "fp16" else 1.0
+    gl = GpuLayer(L)
+    found = torch.zeros(1, dtype=torch.int32, device="cuda")
+    la.check_gradients(gl.grads, found, grad_unscale=unscale)
+    torch.cuda.synchronize()
+    want = oracle.check_finite(oracle_tensors(L), dtype=dtype, unscale=unscale)
+    assert int(found.item()) == want
+    assert want == (0 if inject is None else 1)
+    gl.free()
+
+
+def test_every_fp16_pattern_through_the_check():
+    n = 65536
+    w = synth.Workload(name="check_all", seed=3200, tensors=(("x", n),), replicas=1,
+                       grad_dtype="fp16", step=1)
+    L = synth.make_layer(w)
+    gl = GpuLayer(L)
+    for lo, hi, want in ((0, 0x7C00, 0), (0x7C00, 0x8000, 1), (0x8000, 0xFC00, 0),
+                         (0xFC00, 0x10000, 1)):
+        bits = np.zeros(n, np.uint16)
+        bits[: hi - lo] = np.arange(lo, hi, dtype=np.uint32).astype(np.uint16)
+        g = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.float16)
+        found = torch.zeros(1, dtype=torch.int32, device="cuda")
+        la.check_gradients([[g]], found)
+        torch.cuda.synchronize()
+        assert int(found.item()) == want, (hex(lo), hex(hi))
+    gl.free()
+
+
+def test_gated_step_runs_when_clear_and_skips_when_set():
+    w = ragged(2, with_flag=True)
+    log("case gated")
+    L = synth.make_layer(w)
+    gl = GpuLayer(L)
+    skip = torch.zeros(1, dtype=torch.int32, device="cuda")
+    la.step_gated(gl.params, gl.grads, skip, step=w.step, overflow_flag=gl.flag, **w.hyper)
+    ts = oracle_tensors(L)
+    oracle_step(L, ts)
+    after_one = gl.download()
+    compare(after_one, ts, label="gated_clear")
+    skip.fill_(1)
+    gl.flag.fill_(0)
+    la.step_gated(gl.params, gl.grads, skip, step=w.step + 1, overflow_flag=gl.flag, **w.hyper)
+    after_skip = gl.download()
+    for f in ("master", "exp_avg", "exp_avg_sq", "weight_out"):
+        for a, b in zip(after_one[f], after_skip[f]):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f
+    assert after_skip["flag"] == 0
+    gl.free()
+
+
+def test_check_then_gated_steps_over_two_layers_without_host_sync():
+    """Loss-scaling flow: one flag for the whole step; the check runs over
+    every layer first, then every layer's gated update; one layer overflows,
+    so no layer changes."""
+    log("case two layers gated")
+    layers = []
+    for k in range(2):
+        w = ragged(2, "fp16", seed=3300 + 10 * k, grad_prescale=1024.0, unscale=1 / 1024)
+        L = synth.make_layer(w)
+        if k == 1:
+            L.grad(0, 7)[123] = 0x7C00   # +Inf in the second layer
+        layers.append((w, L, GpuLayer(L)))
+    found = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for w, L, gl in layers:
+        la.check_gradients(gl.grads, found, grad_unscale=w.unscale)
+    before = [gl.download() for _, _, gl in layers]
+    for w, L, gl in layers:
+        la.step_gated(gl.params, gl.grads, found, step=w.step, grad_unscale=w.unscale,
+                      **w.hyper)
+    torch.cuda.synchronize()
+    assert int(found.item()) == 1
+    for (w, L, gl), b in zip(layers, before):
+        a = gl.download()
+        for f in ("master", "exp_avg", "exp_avg_sq", "weight_out"):
+            for x, y in zip(a[f], b[f]):
+                assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), f
+        gl.free()
