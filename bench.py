@@ -178,6 +178,69 @@ def copy_reference(torch, mib: int = 2048, reps: int = 10):
             "kernel": "Tensor.copy_ (device copy)"}
 
 
+def time_launches(torch, fn, reps=10, warm=2):
+    """Mean milliseconds of fn() over reps, HIP events on the current stream."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return statistics.fmean(a.elapsed_time(b) for a, b in ev)
+
+
+def extras(torch, la, w, params, grads, t0):
+    """The neighbouring entry points on the same resident layer, timed after
+    the main region: the layer released in 64 MiB gradient chunks through the
+    range entry point, the finite-check pre-pass, check + gated step, and the
+    FP16 and no compute copies."""
+    n = w.numel
+    t = [t0]
+
+    def hp():
+        t[0] += 1
+        return dict(step=t[0], grad_unscale=w.unscale, **w.hyper)
+
+    out = {}
+    chunk = (64 << 20) // 2  # elements of one 64 MiB chunk of a 16-bit gradient replica
+
+    def by_chunks():
+        for lo in range(0, n, chunk):
+            la.step_range(params, grads, lo, min(n, lo + chunk), **hp())
+
+    ms_whole = time_launches(torch, lambda: la.step(params, grads, **hp()))
+    ms = time_launches(torch, by_chunks)
+    out["range_64MiB_chunks"] = {"chunks": -(-n // chunk), "ms": ms, "whole_layer_ms": ms_whole,
+                                 "overhead": ms / ms_whole - 1.0,
+                                 "gbs": w.traffic_bytes / ms / 1e6}
+    found = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    ms = time_launches(torch, lambda: la.check_gradients(grads, found, grad_unscale=w.unscale))
+    out["check_gradients"] = {"ms": ms, "bytes_per_param": 2 * w.replicas,
+                              "gbs": 2 * w.replicas * n / ms / 1e6}
+
+    def gated():
+        found.zero_()
+        la.check_gradients(grads, found, grad_unscale=w.unscale)
+        la.step_gated(params, grads, found, **hp())
+
+    ms = time_launches(torch, gated)
+    out["check_then_gated_step"] = {"ms": ms, "bytes_per_param": 4 * w.replicas + 26,
+                                    "gbs": (4 * w.replicas + 26) * n / ms / 1e6}
+    as_fp16 = [(p, m, v, wb.view(torch.float16)) for p, m, v, wb in params]
+    ms = time_launches(torch, lambda: la.step(as_fp16, grads, **hp()))
+    out["fp16_compute_copy"] = {"ms": ms, "gbs": w.traffic_bytes / ms / 1e6}
+    no_copy = [(p, m, v, None) for p, m, v, _ in params]
+    ms = time_launches(torch, lambda: la.step(no_copy, grads, **hp()))
+    out["no_compute_copy"] = {"ms": ms, "bytes_per_param": 2 * w.replicas + 24,
+                              "gbs": (2 * w.replicas + 24) * n / ms / 1e6}
+    return out
+
+
 def calibrate_copy(mib: int, reps: int):
     """A plain device-to-device copy of known size, for scaling the HBM byte
     counters (run under rocprofv3 --pmc)."""
@@ -200,6 +263,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the neighbouring entry points timed after the main region")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -306,6 +371,7 @@ def main():
                      "min_launch_ms": min(launch_ms), "max_launch_ms": max(launch_ms)},
         "overflow_flag_first_step": flag_first,
         "hbm_copy_reference": copy_reference(torch),
+        "extras": None if args.no_extras else extras(torch, la, w, params, grads, t),
         "cpu_baseline": None,
     }
     if first is not None:
