@@ -238,6 +238,20 @@ def extras(torch, la, w, params, grads, t0):
     ms = time_launches(torch, lambda: la.step(no_copy, grads, **hp()))
     out["no_compute_copy"] = {"ms": ms, "bytes_per_param": 2 * w.replicas + 24,
                               "gbs": (2 * w.replicas + 24) * n / ms / 1e6}
+    # Host-resident state: master, m, v in pinned host memory; gradients and
+    # the compute copy stay in HBM. 24 B/param cross the host link.
+    host = []
+    for p, m, v, wb in params:
+        hp_, hm, hv = (torch.empty(x.shape, dtype=x.dtype, pin_memory=True) for x in (p, m, v))
+        hp_.copy_(p)
+        hm.copy_(m)
+        hv.copy_(v)
+        host.append((hp_, hm, hv, wb))
+    ms = time_launches(torch, lambda: la.step(host, grads, **hp()), reps=3, warm=1)
+    out["host_resident_state"] = {"ms": ms, "gparams": n / ms / 1e6,
+                                  "host_link_bytes_per_param": 24,
+                                  "host_link_gbs": 24 * n / ms / 1e6}
+    del host
     return out
 
 

@@ -39,10 +39,15 @@
  *    sqrt(1-beta2^t), eps, 1-lr*weight_decay and grad_unscale are computed
  *    on the host in double and rounded to FP32 once per call.
  *
- * Memory and ownership: every buffer is caller-owned device memory of the
- * current HIP device. The library never allocates, never synchronises and
- * keeps no pointer after a call returns. Calls are asynchronous on the given
- * stream; buffers must stay alive until the stream reaches the work.
+ * Memory and ownership: every buffer is caller-owned memory the current HIP
+ * device can address: its own memory, or pinned host memory mapped for it
+ * (hipHostMalloc; pass the device-side address, hipHostGetDevicePointer).
+ * With the master, m and v in pinned host memory the state stays host-
+ * resident, as in the pages' setting ("SlideDP", 前置知识: host-resident
+ * layer streaming), and the kernel streams it over the host link. The
+ * library never allocates, never synchronises and keeps no pointer after a
+ * call returns. Calls are asynchronous on the given stream; buffers must
+ * stay alive until the stream reaches the work.
  *
  * Thread safety: no global mutable state apart from a thread-local error
  * message and a per-device cache of the compute-unit count.

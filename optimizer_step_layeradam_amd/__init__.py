@@ -68,6 +68,51 @@ class LayerAdamError(RuntimeError):
 
 
 _lib = None
+_hip = None
+
+
+class _PointerAttributes(ctypes.Structure):  # hipPointerAttribute_t
+    _fields_ = [("type", ctypes.c_int),
+                ("device", ctypes.c_int),
+                ("devicePointer", ctypes.c_void_p),
+                ("hostPointer", ctypes.c_void_p),
+                ("isManaged", ctypes.c_int),
+                ("allocationFlags", ctypes.c_uint)]
+
+
+_HIP_MEMORY_HOST, _HIP_MEMORY_DEVICE = 1, 2
+
+
+def _hip_runtime():
+    """The HIP runtime already mapped into the process (torch's)."""
+    global _hip
+    if _hip is None:
+        with open("/proc/self/maps") as f:
+            paths = [line.split()[-1] for line in f if "libamdhip64" in line]
+        if not paths:
+            raise RuntimeError("no HIP runtime loaded")
+        _hip = ctypes.CDLL(paths[0])
+        _hip.hipPointerGetAttributes.argtypes = [ctypes.POINTER(_PointerAttributes),
+                                                 ctypes.c_void_p]
+        _hip.hipPointerGetAttributes.restype = ctypes.c_int
+    return _hip
+
+
+def device_address(t) -> int:
+    """Address the kernel may use for tensor t: its data pointer for a CUDA
+    tensor; for a pinned (page-locked) host tensor, the device-side address of
+    the mapping HIP made when it was allocated. Anything else is refused."""
+    if t.is_cuda:
+        return t.data_ptr()
+    if not t.is_pinned():
+        raise TypeError("host tensors must be pinned (page-locked, e.g. pin_memory=True)")
+    ptr = t.data_ptr()
+    attr = _PointerAttributes()
+    rc = _hip_runtime().hipPointerGetAttributes(ctypes.byref(attr), ctypes.c_void_p(ptr))
+    if rc != 0 or attr.type != _HIP_MEMORY_HOST or not attr.devicePointer:
+        raise TypeError(f"pinned host memory at {ptr:#x} is not mapped for the GPU "
+                        f"(hipPointerGetAttributes rc={rc}, type={attr.type})")
+    return attr.devicePointer + (ptr - (attr.hostPointer or ptr))
 
 
 def _single_hip_runtime() -> None:
@@ -252,22 +297,22 @@ def _describe(params, grads, need_state: bool = True):
             for name, t in (("master", p), ("exp_avg", m), ("exp_avg_sq", v)):
                 if t.dtype != torch.float32:
                     raise TypeError(f"tensor {i}: {name} must be float32, got {t.dtype}")
-                if t.numel() != n or not t.is_contiguous() or not t.is_cuda:
-                    raise ValueError(f"tensor {i}: {name} must be a contiguous CUDA tensor "
+                if t.numel() != n or not t.is_contiguous():
+                    raise ValueError(f"tensor {i}: {name} must be a contiguous tensor "
                                      f"of {n} elements")
-                d[name] = t.data_ptr()
+                d[name] = device_address(t)
             if w is not None:
-                if w.numel() != n or not w.is_contiguous() or not w.is_cuda:
-                    raise ValueError(f"tensor {i}: the compute copy must be a contiguous CUDA "
+                if w.numel() != n or not w.is_contiguous():
+                    raise ValueError(f"tensor {i}: the compute copy must be a contiguous "
                                      f"tensor of {n} elements")
-                d["weight_out"] = w.data_ptr()
+                d["weight_out"] = device_address(w)
         if len(gs) != R:
             raise ValueError(f"tensor {i}: {len(gs)} gradient replicas, expected {R}")
         for g in gs:
-            if g.numel() != n or not g.is_contiguous() or not g.is_cuda:
-                raise ValueError(f"tensor {i}: gradients must be contiguous CUDA tensors "
+            if g.numel() != n or not g.is_contiguous():
+                raise ValueError(f"tensor {i}: gradients must be contiguous tensors "
                                  f"of {n} elements")
-        d["grads"] = [g.data_ptr() for g in gs]
+        d["grads"] = [device_address(g) for g in gs]
         out.append(d)
     return out, R, gd, od
 
@@ -296,7 +341,8 @@ def step(params, grads, *, lr: float, beta1: float, beta2: float, eps: float,
     params: per tensor a tuple (master fp32, exp_avg fp32, exp_avg_sq fp32,
             compute copy), updated/written in place; the compute copy is a
             bfloat16 or float16 tensor (the same for every tensor), or None
-            for no copy.
+            for no copy. Every tensor lives in GPU memory or in pinned host
+            memory (host-resident state, reached over the host link).
     grads:  per tensor a list of R gradient replicas (all bf16 or all fp16).
     overflow_flag: optional int32 CUDA tensor of one element (set to 1 on a
             non-finite aggregated gradient; never cleared).
