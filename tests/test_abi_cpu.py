@@ -290,3 +290,33 @@ def test_no_tensors_or_only_empty_tensors_enqueue_nothing():
     desc, keep = la.make_layer([dict(numel=0), dict(numel=0)], 3, la.GRAD_FP16)
     la.step_raw(desc, la.make_params(**HP))
     assert la.last_error() == ""
+
+
+@host_only
+def test_error_messages_are_per_thread():
+    import threading
+    barrier = threading.Barrier(8)
+    seen = {}
+
+    def worker(k):
+        lib = la.load()
+        bad_r = k % 2 == 0
+        desc, keep = la.make_layer([fake_tensor(0)], 0 if bad_r else 2, la.GRAD_BF16)
+        hp = la.make_params(**dict(HP, step=1 if bad_r else 0))
+        msgs = set()
+        for _ in range(200):
+            barrier.wait() if _ == 0 else None
+            rc = lib.layer_adam_step(ctypes.byref(desc), ctypes.byref(hp), None, None)
+            msgs.add((rc, lib.la_last_error().decode().split(",")[0]))
+        seen[k] = msgs
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    for k, msgs in seen.items():
+        assert len(msgs) == 1, msgs
+        rc, msg = next(iter(msgs))
+        assert rc == 1
+        assert msg.startswith("num_replicas" if k % 2 == 0 else "step"), msg
