@@ -332,7 +332,9 @@ layer_adam_kernel(const KernelArgs<R> a) {
 template <int R, bool FP16>
 __global__ void __launch_bounds__(kBlock)
 check_kernel(const KernelArgs<R> a) {
-  if (*a.flag != 0) return;  // already found: the answer cannot change
+  // Already found (by an earlier layer or by other workgroups of this launch,
+  // hence the atomic read): the answer cannot change.
+  if (__hip_atomic_load(a.flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return;
   const int tid = threadIdx.x;
   const int64_t total_chunks = a.chunk_end[a.count - 1];
   const float u = a.s.u;
