@@ -37,40 +37,47 @@ la_status ok() {
 }
 
 // Per-device launch facts, read once per device: the LDS of one compute
-// unit and the most one workgroup may take. (hipDeviceGetAttribute is cheap;
-// caching keeps the per-call host path to a few hundred nanoseconds.)
+// unit and the most one workgroup may take (the kernels size their LDS
+// reservation from them). hipDeviceGetAttribute is cheap; caching keeps the
+// per-call host path to a few hundred nanoseconds.
 constexpr int kMaxDevices = 64;
-std::atomic<int> g_lds_reserve[kMaxDevices];  // bytes + 1; 0 = not read yet
+struct DeviceFacts {
+  std::atomic<int> lds_per_cu{-1};   // -1: not read yet
+  std::atomic<int> lds_per_block{-1};
+};
+DeviceFacts g_facts[kMaxDevices];
 
-// LDS to reserve per workgroup so that at most `per_cu` workgroups fit on a
-// compute unit: floor(lds_per_cu / (per_cu + 1/2)), within the per-workgroup
-// limit. 0 (no reservation) when no cap is wanted or the facts are missing.
-int lds_reserve(int device, int per_cu) {
-  if (per_cu <= 0 || device < 0 || device >= kMaxDevices) return 0;
-  const int cached = g_lds_reserve[device].load(std::memory_order_relaxed);
-  if (cached > 0) return cached - 1;
-  int per_cu_bytes = 0, per_block_bytes = 0;
-  int bytes = 0;
-  if (hipDeviceGetAttribute(&per_cu_bytes, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
-                            device) == hipSuccess &&
-      hipDeviceGetAttribute(&per_block_bytes, hipDeviceAttributeMaxSharedMemoryPerBlock,
-                            device) == hipSuccess &&
-      per_cu_bytes > 0 && per_block_bytes > 0) {
-    bytes = static_cast<int>(2LL * per_cu_bytes / (2LL * per_cu + 1)) / 1024 * 1024;
-    if (bytes > per_block_bytes) bytes = 0;  // cannot cap this way on this device
+void device_facts(int device, int* per_cu, int* per_block) {
+  *per_cu = *per_block = 0;
+  if (device < 0 || device >= kMaxDevices) return;
+  DeviceFacts& f = g_facts[device];
+  int a = f.lds_per_cu.load(std::memory_order_relaxed);
+  int b = f.lds_per_block.load(std::memory_order_relaxed);
+  if (a < 0 || b < 0) {
+    a = b = 0;
+    if (hipDeviceGetAttribute(&a, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                              device) != hipSuccess)
+      a = 0;
+    if (hipDeviceGetAttribute(&b, hipDeviceAttributeMaxSharedMemoryPerBlock, device) !=
+        hipSuccess)
+      b = 0;
+    f.lds_per_block.store(b, std::memory_order_relaxed);
+    f.lds_per_cu.store(a, std::memory_order_relaxed);
   }
-  g_lds_reserve[device].store(bytes + 1, std::memory_order_relaxed);
-  return bytes;
+  *per_cu = a;
+  *per_block = b;
 }
 
-// Workgroups resident per compute unit. LAYERADAM_WORKGROUPS_PER_CU (0..64,
-// read once) overrides the built-in target; 0 removes the cap.
-int workgroups_per_cu() {
+// Resident workgroups per compute unit: LAYERADAM_WORKGROUPS_PER_CU (0..64,
+// read once) overrides every kernel's own default; 0 removes the cap; -1
+// (unset or unparsable) keeps the defaults.
+int workgroups_per_cu_override() {
   static const int value = [] {
     const char* env = std::getenv("LAYERADAM_WORKGROUPS_PER_CU");
-    if (env == nullptr) return la::target_workgroups_per_cu();
-    const int v = std::atoi(env);
-    return (v >= 0 && v <= 64) ? v : la::target_workgroups_per_cu();
+    if (env == nullptr || *env == '\0') return -1;
+    char* end = nullptr;
+    const long v = std::strtol(env, &end, 10);
+    return (*end == '\0' && v >= 0 && v <= 64) ? static_cast<int>(v) : -1;
   }();
   return value;
 }
@@ -261,7 +268,7 @@ la_status enqueue(const la_layer_desc* layer, Mode mode, const la::Scalars& s, i
   int pending = 0;
   int launches = 0;
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
-  la::LaunchShape shape{0, 0};
+  la::LaunchShape shape{0, 0, 0, -1};
   const bool fp16 = layer->grad_dtype == LA_GRAD_FP16;
   const bool out = mode == Mode::kUpdate && layer->out_dtype != LA_OUT_NONE;
 
@@ -273,7 +280,8 @@ la_status enqueue(const la_layer_desc* layer, Mode mode, const la::Scalars& s, i
       if (e != hipSuccess)
         return fail(LA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
       shape.grid_cap = kMaxGrid;
-      shape.lds_bytes = lds_reserve(device, workgroups_per_cu());
+      device_facts(device, &shape.lds_per_cu, &shape.lds_per_block);
+      shape.wg_per_cu = workgroups_per_cu_override();
     }
     hipError_t e = mode == Mode::kUpdate
                        ? la::launch_layer_adam(batch, pending, layer->num_replicas, fp16,

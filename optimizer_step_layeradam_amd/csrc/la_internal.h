@@ -39,13 +39,12 @@ struct TensorArgs {
 };
 
 struct LaunchShape {
-  int grid_cap;   // upper bound on workgroups of one launch
-  int lds_bytes;  // LDS reserved per workgroup (unused by the kernel); caps
-                  // how many workgroups a compute unit holds at once
+  int grid_cap;        // upper bound on workgroups of one launch
+  int lds_per_cu;      // LDS bytes of one compute unit (0: unknown)
+  int lds_per_block;   // most LDS one workgroup may take (0: unknown)
+  int wg_per_cu;       // resident workgroups per compute unit to aim for;
+                       // -1: each kernel's own default, 0: no cap
 };
-
-// Workgroups resident per compute unit that the launch aims for.
-int target_workgroups_per_cu();
 
 // Enqueue the update of `count` (1..kTensorsPerLaunch) tensors in one launch.
 // flag: overflow flag or null; skip: device flag that makes the kernel a

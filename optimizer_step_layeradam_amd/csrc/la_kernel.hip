@@ -69,7 +69,16 @@ namespace {
 #define LA_WAVE_CONTIG 1   // 1: each wave's tiles are adjacent in memory
 #endif
 #ifndef LA_WORKGROUPS_PER_CU
-#define LA_WORKGROUPS_PER_CU 2  // resident workgroups per compute unit (0: no cap)
+#define LA_WORKGROUPS_PER_CU 2  // update: resident workgroups per compute unit (0: no cap)
+#endif
+// The finite check only reads: more requests in flight help it (measured
+// 7.1 TB/s with 8 tiles per chunk and no residency cap, against 5.5 TB/s
+// with the update's shape).
+#ifndef LA_CHECK_TILE_UNROLL
+#define LA_CHECK_TILE_UNROLL 8  // finite check: tiles per chunk
+#endif
+#ifndef LA_CHECK_WORKGROUPS_PER_CU
+#define LA_CHECK_WORKGROUPS_PER_CU 0  // finite check: resident workgroups per compute unit
 #endif
 
 constexpr int kBlock = LA_BLOCK;        // threads per workgroup
@@ -77,6 +86,8 @@ constexpr int kVec = LA_TILE_VEC;       // consecutive elements per thread per t
 constexpr int kUnroll = LA_TILE_UNROLL; // tiles per chunk
 constexpr int kChunk = kBlock * kVec * kUnroll;
 constexpr int kQuads = kVec / 4;        // 16-byte FP32 vectors per array per tile
+constexpr int kCheckUnroll = LA_CHECK_TILE_UNROLL;
+constexpr int kCheckChunk = kBlock * kVec * kCheckUnroll;
 static_assert(kVec == 4 || kVec == 8, "4 or 8 elements per thread per tile");
 static_assert(kBlock % 64 == 0 && kBlock <= 1024, "whole waves");
 
@@ -203,12 +214,13 @@ __device__ __forceinline__ float aggregate_one(const uint16_t* const (&g)[R], in
   return x * u;
 }
 
-// Element offset, within its chunk, of thread tid's first element in tile u.
-// Tile-major: tile u covers [u * kBlock * kVec, (u + 1) * kBlock * kVec).
-// Wave-contiguous: wave w owns kUnroll adjacent runs of 64 * kVec elements.
+// Element offset, within its chunk of TILES tiles, of thread tid's first
+// element in tile u. Tile-major: tile u covers [u, u + 1) * kBlock * kVec.
+// Wave-contiguous: wave w owns TILES adjacent runs of 64 * kVec elements.
+template <int TILES = kUnroll>
 __device__ __forceinline__ uint32_t tile_offset(int u, int tid) {
   if constexpr (LA_WAVE_CONTIG) {
-    return static_cast<uint32_t>((((tid >> 6) * kUnroll + u) * 64 + (tid & 63)) * kVec);
+    return static_cast<uint32_t>((((tid >> 6) * TILES + u) * 64 + (tid & 63)) * kVec);
   } else {
     return static_cast<uint32_t>((u * kBlock + tid) * kVec);
   }
@@ -345,30 +357,30 @@ check_kernel(const KernelArgs<R> a) {
   for (int64_t c = blockIdx.x; c < total_chunks; c += gridDim.x) {
     locate(a, c, t, first_chunk_of_t);
     const KernelTensor<R>& T = a.t[t];
-    const int64_t base = (c - first_chunk_of_t) * kChunk;
+    const int64_t base = (c - first_chunk_of_t) * kCheckChunk;
     const int64_t n = T.numel;
     const uint16_t* g[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) g[r] = T.g[r] + base;
 
-    if (base + kChunk <= n) {
-      half_words G[kUnroll][R];
+    if (base + kCheckChunk <= n) {
+      half_words G[kCheckUnroll][R];
 #pragma unroll
-      for (int tile = 0; tile < kUnroll; ++tile) {
-        const uint32_t off = tile_offset(tile, tid);
+      for (int tile = 0; tile < kCheckUnroll; ++tile) {
+        const uint32_t off = tile_offset<kCheckUnroll>(tile, tid);
 #pragma unroll
         for (int r = 0; r < R; ++r)
           G[tile][r] = load_stream(reinterpret_cast<const half_words*>(g[r] + off));
       }
 #pragma unroll
-      for (int tile = 0; tile < kUnroll; ++tile)
+      for (int tile = 0; tile < kCheckUnroll; ++tile)
 #pragma unroll
         for (int k = 0; k < kVec; ++k)
           bad |= !__builtin_isfinite(aggregate<R, FP16>(G[tile], k, u));
     } else {
       const int64_t left = n - base;
 #pragma unroll 1
-      for (int tile = 0; tile < kUnroll; ++tile) {
+      for (int tile = 0; tile < kCheckUnroll; ++tile) {
 #pragma unroll
         for (int k = 0; k < kVec; ++k) {
           const int64_t i = static_cast<int64_t>((tile * kBlock + tid) * kVec + k);
@@ -382,7 +394,7 @@ check_kernel(const KernelArgs<R> a) {
 
 // ---- launch --------------------------------------------------------------------
 template <int R>
-int64_t fill_args(KernelArgs<R>& a, const TensorArgs* ts, int count) {
+int64_t fill_args(KernelArgs<R>& a, const TensorArgs* ts, int count, int64_t chunk) {
   int64_t chunks = 0;
   for (int i = 0; i < count; ++i) {
     a.t[i].p = ts[i].p;
@@ -391,19 +403,29 @@ int64_t fill_args(KernelArgs<R>& a, const TensorArgs* ts, int count) {
     a.t[i].w = ts[i].w;
     for (int r = 0; r < R; ++r) a.t[i].g[r] = ts[i].g[r];
     a.t[i].numel = ts[i].numel;
-    chunks += (ts[i].numel + kChunk - 1) / kChunk;
+    chunks += (ts[i].numel + chunk - 1) / chunk;
     a.chunk_end[i] = chunks;
   }
   a.count = count;
   return chunks;
 }
 
-hipError_t launch(const void* kernel, void* args, int64_t chunks, hipStream_t stream,
+// LDS to reserve per workgroup so that at most `per_cu` workgroups fit on a
+// compute unit: floor(lds_per_cu / (per_cu + 1/2)) in whole KiB, within the
+// per-workgroup limit; 0 (no reservation) for no cap or unknown facts.
+int lds_reservation(const LaunchShape& shape, int default_per_cu) {
+  const int per_cu = shape.wg_per_cu < 0 ? default_per_cu : shape.wg_per_cu;
+  if (per_cu <= 0 || shape.lds_per_cu <= 0 || shape.lds_per_block <= 0) return 0;
+  const int bytes = static_cast<int>(2LL * shape.lds_per_cu / (2LL * per_cu + 1)) / 1024 * 1024;
+  return bytes <= shape.lds_per_block ? bytes : 0;
+}
+
+hipError_t launch(const void* kernel, void* args, int64_t chunks, int lds, hipStream_t stream,
                   const LaunchShape& shape) {
   const int64_t grid = chunks < shape.grid_cap ? chunks : shape.grid_cap;  // >= 1
   void* params[] = {args};
   return hipLaunchKernel(kernel, dim3(static_cast<unsigned>(grid)), dim3(kBlock), params,
-                         static_cast<unsigned>(shape.lds_bytes), stream);
+                         static_cast<unsigned>(lds), stream);
 }
 
 template <int R, bool FP16, bool FLAG, int OUT>
@@ -411,12 +433,12 @@ hipError_t launch_update_typed(const TensorArgs* ts, int count, const Scalars& s
                                int32_t* flag, const int32_t* skip, hipStream_t stream,
                                const LaunchShape& shape) {
   KernelArgs<R> a = {};
-  const int64_t chunks = fill_args(a, ts, count);
+  const int64_t chunks = fill_args(a, ts, count, kChunk);
   a.s = s;
   a.flag = flag;
   a.skip = skip;
   return launch(reinterpret_cast<const void*>(&layer_adam_kernel<R, FP16, FLAG, OUT>), &a,
-                chunks, stream, shape);
+                chunks, lds_reservation(shape, LA_WORKGROUPS_PER_CU), stream, shape);
 }
 
 template <int R, bool FP16, int OUT>
@@ -451,19 +473,18 @@ template <int R>
 hipError_t launch_check_r(const TensorArgs* ts, int count, bool fp16, float u, int32_t* flag,
                           hipStream_t stream, const LaunchShape& shape) {
   KernelArgs<R> a = {};
-  const int64_t chunks = fill_args(a, ts, count);
+  const int64_t chunks = fill_args(a, ts, count, kCheckChunk);
   a.s.u = u;
   a.flag = flag;
   const void* k = fp16 ? reinterpret_cast<const void*>(&check_kernel<R, true>)
                        : reinterpret_cast<const void*>(&check_kernel<R, false>);
-  return launch(k, &a, chunks, stream, shape);
+  return launch(k, &a, chunks, lds_reservation(shape, LA_CHECK_WORKGROUPS_PER_CU), stream,
+                shape);
 }
 
 }  // namespace
 
-int64_t chunk_elements() { return kChunk; }
-
-int target_workgroups_per_cu() { return LA_WORKGROUPS_PER_CU; }
+int64_t chunk_elements() { return kChunk < kCheckChunk ? kChunk : kCheckChunk; }
 
 hipError_t launch_layer_adam(const TensorArgs* tensors, int count, int replicas, bool fp16,
                              int out_dtype, const Scalars& s, int32_t* flag,
