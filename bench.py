@@ -144,6 +144,47 @@ def cpu_baseline(L, first, budget_s: float):
     }
 
 
+def cpu_parallel(L, threads: int):
+    """Context only: the same oracle over disjoint slices of the whole layer
+    on `threads` host threads (ctypes releases the GIL), one step, wall time.
+    Comparable in kind to the pages' multi-core host Adam."""
+    import threading
+    import numpy as np
+    import oracle
+    w = L.workload
+    work = []
+    for i, (_, n) in enumerate(w.tensors):
+        for a in range(0, n, 1 << 22):
+            b = min(n, a + (1 << 22))
+            work.append(oracle.Tensor(L.master[i][a:b].copy(), L.exp_avg[i][a:b].copy(),
+                                      L.exp_avg_sq[i][a:b].copy(), np.zeros(b - a, np.uint16),
+                                      [np.ascontiguousarray(L.grad(r, i)[a:b])
+                                       for r in range(w.replicas)]))
+    lock = threading.Lock()
+    queue = list(range(len(work)))
+
+    def run():
+        while True:
+            with lock:
+                if not queue:
+                    return
+                k = queue.pop()
+            oracle.step([work[k]], dtype=w.grad_dtype, step=w.step, unscale=w.unscale,
+                        **w.hyper)
+
+    pool = [threading.Thread(target=run) for _ in range(threads)]
+    t0 = time.perf_counter()
+    for t in pool:
+        t.start()
+    for t in pool:
+        t.join()
+    seconds = time.perf_counter() - t0
+    gps = w.numel / seconds / 1e9
+    return {"value": gps, "unit": "Gparam/s", "cores": threads, "kind": "oracle, disjoint slices",
+            "sample": f"the whole layer ({w.numel} parameters), one step", "seconds": seconds,
+            "hbm_model_gbs": gps * w.bytes_per_param}
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -391,6 +432,10 @@ def main():
     if first is not None:
         log("bench: CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(L, first, args.cpu_seconds)
+        threads = min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity")
+                      else (os.cpu_count() or 1))
+        log(f"bench: CPU oracle on {threads} threads (context)")
+        out["cpu_parallel_context"] = cpu_parallel(L, threads)
     print(json.dumps(out), flush=True)
 
 
