@@ -103,6 +103,10 @@ def device_address(t) -> int:
     tensor; for a pinned (page-locked) host tensor, the device-side address of
     the mapping HIP made when it was allocated. Anything else is refused."""
     if t.is_cuda:
+        import torch
+        if t.device.index != torch.cuda.current_device():
+            raise ValueError(f"tensor on {t.device}, but the current device is "
+                             f"cuda:{torch.cuda.current_device()}")
         return t.data_ptr()
     if not t.is_pinned():
         raise TypeError("host tensors must be pinned (page-locked, e.g. pin_memory=True)")

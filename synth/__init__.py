@@ -9,7 +9,7 @@ from __future__ import annotations
 import ctypes
 import os
 import subprocess
-from dataclasses import dataclass
+from dataclasses import dataclass, replace  # noqa: F401  (replace: Workload variants)
 from typing import List, Optional
 
 import numpy as np

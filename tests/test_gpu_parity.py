@@ -168,6 +168,25 @@ def test_hyperparameter_variants(case):
     run_case(w, **hp)
 
 
+def test_a_hundred_consecutive_steps():
+    """t = 1..100 from zero moments on a reduced Qwen3-4B layer; the state is
+    compared with the oracle's after every 25 steps (no drift, no stale
+    element)."""
+    w = synth.replace(synth.shrink(synth.WORKLOADS["qwen3_4b_layer"], 256), step=1,
+                      m_std=None, v_high=None)
+    log(f"case 100 steps N={w.numel}")
+    L = synth.make_layer(w)
+    gl = GpuLayer(L)
+    ts = oracle_tensors(L)
+    for t in range(1, 101):
+        gl.step(t=t)
+        oracle_step(L, ts, t=t)
+        if t % 25 == 0:
+            rep = compare(gl.download(), ts, label=f"t={t}")
+            assert rep.max_ulp == 0
+    gl.free()
+
+
 def test_three_consecutive_steps():
     w = synth.Workload(name="three_steps", seed=2600, tensors=RAGGED, replicas=2,
                        grad_dtype="bf16", step=1, m_std=None, v_high=None)
