@@ -185,6 +185,22 @@ LA_API la_status layer_adam_step_gated(const la_layer_desc *layer,
                                        int32_t *overflow_flag,
                                        void *hip_stream);
 
+/* layer_adam_step with the step count t read from device memory when the
+ * kernel runs: *step_on_device (an 8-byte-aligned int64 in device memory;
+ * may not be NULL) instead of hp->step, which is ignored. The two constants
+ * that depend on t, lr/(1 - beta1^t) and sqrt(1 - beta2^t), are then formed
+ * on the GPU in double and rounded to FP32 once, as the host does for the
+ * other entry points (the device pow() may differ from the host's in the
+ * last double ulp, which can move the master by at most about one FP32
+ * ulp). A value below 1 makes the launch a no-op. This is the form to
+ * capture in a HIP graph: the caller advances the device counter (e.g. with
+ * a captured increment) and every replay applies the next step. */
+LA_API la_status layer_adam_step_device_step(const la_layer_desc *layer,
+                                             const la_adam_params *hp,
+                                             const int64_t *step_on_device,
+                                             int32_t *overflow_flag,
+                                             void *hip_stream);
+
 /* Bytes of mixed-precision Adam state the layer stands for: 16 per
  * parameter (2 BF16 weight + 2 gradient + 4 FP32 master + 8 FP32 m and v).
  * -1 if the descriptor is invalid. Host only. */

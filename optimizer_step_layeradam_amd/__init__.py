@@ -30,7 +30,7 @@ OUT_BF16, OUT_FP16, OUT_NONE = 0, 1, 2
 
 # Exported symbols, as declared in include/layeradam.h.
 EXPORTS = ("layer_adam_step", "layer_adam_step_range", "layer_adam_step_gated",
-           "la_check_gradients", "la_state_bytes", "la_traffic_bytes", "la_last_error",
+           "layer_adam_step_device_step", "la_check_gradients", "la_state_bytes", "la_traffic_bytes", "la_last_error",
            "la_version")
 
 
@@ -158,6 +158,10 @@ def load(path: Optional[str] = None):
     lib.layer_adam_step_gated.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(AdamParams),
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.layer_adam_step_gated.restype = ctypes.c_int
+    lib.layer_adam_step_device_step.argtypes = [ctypes.POINTER(LayerDesc),
+                                                ctypes.POINTER(AdamParams), ctypes.c_void_p,
+                                                ctypes.c_void_p, ctypes.c_void_p]
+    lib.layer_adam_step_device_step.restype = ctypes.c_int
     lib.la_check_gradients.argtypes = [ctypes.POINTER(LayerDesc), ctypes.c_double,
                                        ctypes.c_void_p, ctypes.c_void_p]
     lib.la_check_gradients.restype = ctypes.c_int
@@ -237,6 +241,15 @@ def step_gated_raw(desc: LayerDesc, params: AdamParams, skip_if_nonzero: int,
     _raise_on(lib.layer_adam_step_gated(ctypes.byref(desc), ctypes.byref(params),
                                         skip_if_nonzero or None, overflow_flag or None,
                                         stream or None), lib)
+
+
+def step_device_step_raw(desc: LayerDesc, params: AdamParams, step_on_device: int,
+                         overflow_flag: int = 0, stream: int = 0) -> None:
+    """layer_adam_step_device_step on raw descriptors (params.step ignored)."""
+    lib = load()
+    _raise_on(lib.layer_adam_step_device_step(ctypes.byref(desc), ctypes.byref(params),
+                                              step_on_device or None, overflow_flag or None,
+                                              stream or None), lib)
 
 
 def check_gradients_raw(desc: LayerDesc, grad_unscale: float, found_nonfinite: int,
@@ -380,6 +393,23 @@ def step_gated(params, grads, skip_if_nonzero, *, lr: float, beta1: float, beta2
     hp = make_params(lr, beta1, beta2, eps, weight_decay, step, grad_unscale)
     step_gated_raw(desc, hp, _flag_ptr(skip_if_nonzero), _flag_ptr(overflow_flag),
                    _stream_ptr(stream))
+    del keep
+
+
+def step_device_step(params, grads, step_on_device, *, lr: float, beta1: float, beta2: float,
+                     eps: float, weight_decay: float, grad_unscale: float = 1.0,
+                     overflow_flag=None, stream=None) -> None:
+    """The update with t read on the GPU from the int64 CUDA scalar
+    ``step_on_device`` when the kernel runs (graph-capturable: advance the
+    counter on the device between replays)."""
+    import torch
+    if step_on_device.dtype != torch.int64 or not step_on_device.is_cuda:
+        raise TypeError("step_on_device must be an int64 CUDA tensor")
+    tensors, R, gd, od = _describe(params, grads)
+    desc, keep = make_layer(tensors, R, gd, od)
+    hp = make_params(lr, beta1, beta2, eps, weight_decay, 1, grad_unscale)
+    step_device_step_raw(desc, hp, device_address(step_on_device), _flag_ptr(overflow_flag),
+                         _stream_ptr(stream))
     del keep
 
 

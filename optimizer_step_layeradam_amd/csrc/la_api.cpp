@@ -162,7 +162,7 @@ bool overlaps(const Range& a, const Range& b) { return a.begin < b.end && b.begi
 // that is only read (gradients, the skip flag). Sort the written ranges;
 // check neighbours, then look every read range up by binary search.
 la_status check_aliasing(const la_layer_desc* layer, Mode mode, const int32_t* flag,
-                         const int32_t* skip) {
+                         const int32_t* skip, const int64_t* step = nullptr) {
   std::vector<Range> written;
   std::vector<Range> read;
   const bool state = mode == Mode::kUpdate;
@@ -192,6 +192,10 @@ la_status check_aliasing(const la_layer_desc* layer, Mode mode, const int32_t* f
   if (skip != nullptr) {
     const uintptr_t b = reinterpret_cast<uintptr_t>(skip);
     read.push_back({b, b + 4, "skip_if_nonzero", -1});
+  }
+  if (step != nullptr) {
+    const uintptr_t b = reinterpret_cast<uintptr_t>(step);
+    read.push_back({b, b + 8, "step_on_device", -1});
   }
   std::sort(written.begin(), written.end(),
             [](const Range& a, const Range& b) { return a.begin < b.begin; });
@@ -262,8 +266,9 @@ int64_t total_numel(const la_layer_desc* layer) {
 // the next multiple of 8 (at most 7 elements, so always the element-wise
 // path of the kernel) becomes its own entry, and the rest starts 16-byte
 // aligned (32 bytes into FP32 arrays, 16 into 16-bit arrays).
-la_status enqueue(const la_layer_desc* layer, Mode mode, const la::Scalars& s, int64_t begin,
-                  int64_t end, int32_t* flag, const int32_t* skip, void* hip_stream) {
+la_status enqueue(const la_layer_desc* layer, Mode mode, const la::Scalars& s,
+                  const la::DeviceStep& dstep, int64_t begin, int64_t end, int32_t* flag,
+                  const int32_t* skip, void* hip_stream) {
   la::TensorArgs batch[la::kTensorsPerLaunch];
   int pending = 0;
   int launches = 0;
@@ -285,7 +290,8 @@ la_status enqueue(const la_layer_desc* layer, Mode mode, const la::Scalars& s, i
     }
     hipError_t e = mode == Mode::kUpdate
                        ? la::launch_layer_adam(batch, pending, layer->num_replicas, fp16,
-                                               layer->out_dtype, s, flag, skip, stream, shape)
+                                               layer->out_dtype, s, dstep, flag, skip, stream,
+                                               shape)
                        : la::launch_check_gradients(batch, pending, layer->num_replicas, fp16,
                                                     s.u, flag, stream, shape);
     if (e != hipSuccess)
@@ -316,7 +322,7 @@ la_status enqueue(const la_layer_desc* layer, Mode mode, const la::Scalars& s, i
     if (lo >= hi) continue;
     int64_t first = lo - offset + t.numel;  // element within the tensor
     int64_t count = hi - lo;
-    const int64_t head = std::min(count, (8 - first % 8) % 8);
+    const int64_t head = std::min(count, (8 - first % 8) % 8);  // <= la::kMaxUnalignedEntry
     la_status st;
     if (head > 0) {
       if ((st = add(t, first, head)) != LA_OK) return st;
@@ -332,12 +338,22 @@ la_status enqueue(const la_layer_desc* layer, Mode mode, const la::Scalars& s, i
 
 la_status update(const la_layer_desc* layer, const la_adam_params* hp, int64_t begin,
                  int64_t end, bool whole, int32_t* flag, const int32_t* skip,
-                 void* hip_stream) {
+                 const int64_t* step_on_device, void* hip_stream) {
   la_status st = check_counts(layer);
   if (st != LA_OK) return st;
   if ((st = check_pointers(layer, Mode::kUpdate)) != LA_OK) return st;
   la::Scalars s;
-  if ((st = derive_scalars(hp, &s)) != LA_OK) return st;
+  la::DeviceStep dstep = {nullptr, 0.0, 0.0, 0.0};
+  if (step_on_device != nullptr && hp != nullptr) {
+    if (!aligned(step_on_device, 8))
+      return fail(LA_ERR_MISALIGNED, "step_on_device is not 8-byte aligned");
+    la_adam_params at_one = *hp;  // t comes from the device; check the rest
+    at_one.step = 1;
+    if ((st = derive_scalars(&at_one, &s)) != LA_OK) return st;
+    dstep = {step_on_device, hp->lr, hp->beta1, hp->beta2};
+  } else if ((st = derive_scalars(hp, &s)) != LA_OK) {
+    return st;
+  }
   if (flag != nullptr && !aligned(flag, 4))
     return fail(LA_ERR_MISALIGNED, "overflow_flag is not 4-byte aligned");
   if (skip != nullptr && !aligned(skip, 4))
@@ -351,8 +367,9 @@ la_status update(const la_layer_desc* layer, const la_adam_params* hp, int64_t b
                 static_cast<long long>(begin), static_cast<long long>(end),
                 static_cast<long long>(n));
   }
-  if ((st = check_aliasing(layer, Mode::kUpdate, flag, skip)) != LA_OK) return st;
-  return enqueue(layer, Mode::kUpdate, s, begin, end, flag, skip, hip_stream);
+  if ((st = check_aliasing(layer, Mode::kUpdate, flag, skip, step_on_device)) != LA_OK)
+    return st;
+  return enqueue(layer, Mode::kUpdate, s, dstep, begin, end, flag, skip, hip_stream);
 }
 
 }  // namespace
@@ -361,13 +378,14 @@ extern "C" {
 
 LA_API la_status layer_adam_step(const la_layer_desc* layer, const la_adam_params* hp,
                                  int32_t* overflow_flag, void* hip_stream) {
-  return update(layer, hp, 0, 0, true, overflow_flag, nullptr, hip_stream);
+  return update(layer, hp, 0, 0, true, overflow_flag, nullptr, nullptr, hip_stream);
 }
 
 LA_API la_status layer_adam_step_range(const la_layer_desc* layer, const la_adam_params* hp,
                                        int64_t elem_begin, int64_t elem_end,
                                        int32_t* overflow_flag, void* hip_stream) {
-  return update(layer, hp, elem_begin, elem_end, false, overflow_flag, nullptr, hip_stream);
+  return update(layer, hp, elem_begin, elem_end, false, overflow_flag, nullptr, nullptr,
+                hip_stream);
 }
 
 LA_API la_status layer_adam_step_gated(const la_layer_desc* layer, const la_adam_params* hp,
@@ -375,7 +393,16 @@ LA_API la_status layer_adam_step_gated(const la_layer_desc* layer, const la_adam
                                        int32_t* overflow_flag, void* hip_stream) {
   if (skip_if_nonzero == nullptr)
     return fail(LA_ERR_INVALID_ARGUMENT, "skip_if_nonzero is NULL");
-  return update(layer, hp, 0, 0, true, overflow_flag, skip_if_nonzero, hip_stream);
+  return update(layer, hp, 0, 0, true, overflow_flag, skip_if_nonzero, nullptr, hip_stream);
+}
+
+LA_API la_status layer_adam_step_device_step(const la_layer_desc* layer,
+                                             const la_adam_params* hp,
+                                             const int64_t* step_on_device,
+                                             int32_t* overflow_flag, void* hip_stream) {
+  if (step_on_device == nullptr)
+    return fail(LA_ERR_INVALID_ARGUMENT, "step_on_device is NULL");
+  return update(layer, hp, 0, 0, true, overflow_flag, nullptr, step_on_device, hip_stream);
 }
 
 LA_API la_status la_check_gradients(const la_layer_desc* layer, double grad_unscale,
@@ -391,8 +418,8 @@ LA_API la_status la_check_gradients(const la_layer_desc* layer, double grad_unsc
   if ((st = check_aliasing(layer, Mode::kCheck, found_nonfinite, nullptr)) != LA_OK) return st;
   la::Scalars s = {};
   s.u = static_cast<float>(grad_unscale);
-  return enqueue(layer, Mode::kCheck, s, 0, total_numel(layer), found_nonfinite, nullptr,
-                 hip_stream);
+  return enqueue(layer, Mode::kCheck, s, la::DeviceStep{nullptr, 0.0, 0.0, 0.0}, 0,
+                 total_numel(layer), found_nonfinite, nullptr, hip_stream);
 }
 
 LA_API int64_t la_state_bytes(const la_layer_desc* layer) {
@@ -410,6 +437,6 @@ LA_API int64_t la_traffic_bytes(const la_layer_desc* layer) {
 
 LA_API const char* la_last_error(void) { return g_error; }
 
-LA_API const char* la_version(void) { return "layeradam 0.2.0 gfx950"; }
+LA_API const char* la_version(void) { return "layeradam 0.3.0 gfx950"; }
 
 }  // extern "C"

@@ -17,6 +17,10 @@ constexpr int kOutNone = 2;
 // (about 104 bytes per tensor at R = 8).
 constexpr int kTensorsPerLaunch = 16;
 
+// Longest entry that may start unaligned (the head peeled off an element
+// range that does not start at a multiple of 8 elements).
+constexpr int kMaxUnalignedEntry = 7;
+
 // The FP32 constants of one step, derived on the host.
 struct Scalars {
   float b1, c1;   // beta1, 1 - beta1
@@ -26,6 +30,13 @@ struct Scalars {
   float e;        // eps
   float d;        // 1 - lr * weight_decay
   float u;        // gradient unscale factor
+};
+
+// With the step count in device memory, the kernel derives alpha and q
+// itself from these (the other constants come from the host as usual).
+struct DeviceStep {
+  const int64_t* t;  // null: alpha and q in Scalars are final
+  double lr, beta1, beta2;
 };
 
 // One non-empty tensor, already validated (16-byte aligned, disjoint).
@@ -48,14 +59,14 @@ struct LaunchShape {
 
 // Enqueue the update of `count` (1..kTensorsPerLaunch) tensors in one launch.
 // flag: overflow flag or null; skip: device flag that makes the kernel a
-// no-op when non-zero, or null. A tensor entry with fewer than
-// chunk_elements() elements may have pointers aligned to their element size
-// only (it takes the element-wise path); larger entries need 16-byte
-// alignment of every pointer.
+// no-op when non-zero, or null. An entry of at most kMaxUnalignedEntry
+// elements may have pointers aligned to their element size only (every
+// kernel takes its element-wise path for an entry shorter than one chunk);
+// longer entries need 16-byte alignment of every pointer.
 hipError_t launch_layer_adam(const TensorArgs* tensors, int count, int replicas,
-                             bool fp16, int out_dtype, const Scalars& s, int32_t* flag,
-                             const int32_t* skip, hipStream_t stream,
-                             const LaunchShape& shape);
+                             bool fp16, int out_dtype, const Scalars& s,
+                             const DeviceStep& dstep, int32_t* flag, const int32_t* skip,
+                             hipStream_t stream, const LaunchShape& shape);
 
 // Enqueue the finite check of the aggregated gradients (sum of replicas times
 // unscale) of `count` tensors; sets *flag to 1 if one is +-Inf or NaN.
@@ -63,7 +74,5 @@ hipError_t launch_check_gradients(const TensorArgs* tensors, int count, int repl
                                   bool fp16, float unscale, int32_t* flag,
                                   hipStream_t stream, const LaunchShape& shape);
 
-// Elements one workgroup processes per chunk.
-int64_t chunk_elements();
 
 }  // namespace la

@@ -90,6 +90,8 @@ constexpr int kCheckUnroll = LA_CHECK_TILE_UNROLL;
 constexpr int kCheckChunk = kBlock * kVec * kCheckUnroll;
 static_assert(kVec == 4 || kVec == 8, "4 or 8 elements per thread per tile");
 static_assert(kBlock % 64 == 0 && kBlock <= 1024, "whole waves");
+static_assert(kChunk > kMaxUnalignedEntry && kCheckChunk > kMaxUnalignedEntry,
+              "short unaligned entries must take the element-wise path");
 
 // Native vector types (the non-temporal builtins need them).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -124,6 +126,7 @@ struct KernelArgs {
   Scalars s;
   int32_t* flag;         // overflow / found-non-finite flag, or null
   const int32_t* skip;   // update only: skip everything if *skip != 0; or null
+  DeviceStep dstep;      // update only: step count in device memory, or t == null
   int32_t count;
 };
 
@@ -265,7 +268,16 @@ layer_adam_kernel(const KernelArgs<R> a) {
   if (a.skip != nullptr && *a.skip != 0) return;  // gated step: overflowed, skip
   const int tid = threadIdx.x;
   const int64_t total_chunks = a.chunk_end[a.count - 1];
-  const Scalars s = a.s;
+  Scalars s = a.s;
+  if (a.dstep.t != nullptr) {
+    // Step count in device memory: the bias corrections of AdamW at the
+    // 1-based step t, in double, each constant rounded once to FP32.
+    const int64_t t = *a.dstep.t;
+    if (t < 1) return;
+    const double td = static_cast<double>(t);
+    s.alpha = static_cast<float>(a.dstep.lr / (1.0 - pow(a.dstep.beta1, td)));
+    s.q = static_cast<float>(sqrt(1.0 - pow(a.dstep.beta2, td)));
+  }
   bool bad = false;
 
   int t = 0;
@@ -430,11 +442,12 @@ hipError_t launch(const void* kernel, void* args, int64_t chunks, int lds, hipSt
 
 template <int R, bool FP16, bool FLAG, int OUT>
 hipError_t launch_update_typed(const TensorArgs* ts, int count, const Scalars& s,
-                               int32_t* flag, const int32_t* skip, hipStream_t stream,
-                               const LaunchShape& shape) {
+                               const DeviceStep& dstep, int32_t* flag, const int32_t* skip,
+                               hipStream_t stream, const LaunchShape& shape) {
   KernelArgs<R> a = {};
   const int64_t chunks = fill_args(a, ts, count, kChunk);
   a.s = s;
+  a.dstep = dstep;
   a.flag = flag;
   a.skip = skip;
   return launch(reinterpret_cast<const void*>(&layer_adam_kernel<R, FP16, FLAG, OUT>), &a,
@@ -443,30 +456,30 @@ hipError_t launch_update_typed(const TensorArgs* ts, int count, const Scalars& s
 
 template <int R, bool FP16, int OUT>
 hipError_t launch_update_flag(const TensorArgs* ts, int count, const Scalars& s,
-                              int32_t* flag, const int32_t* skip, hipStream_t stream,
-                              const LaunchShape& shape) {
-  return flag ? launch_update_typed<R, FP16, true, OUT>(ts, count, s, flag, skip, stream, shape)
-              : launch_update_typed<R, FP16, false, OUT>(ts, count, s, flag, skip, stream, shape);
+                              const DeviceStep& d, int32_t* flag, const int32_t* skip,
+                              hipStream_t stream, const LaunchShape& shape) {
+  return flag ? launch_update_typed<R, FP16, true, OUT>(ts, count, s, d, flag, skip, stream, shape)
+              : launch_update_typed<R, FP16, false, OUT>(ts, count, s, d, flag, skip, stream, shape);
 }
 
 template <int R, bool FP16>
 hipError_t launch_update_out(const TensorArgs* ts, int count, int out, const Scalars& s,
-                             int32_t* flag, const int32_t* skip, hipStream_t stream,
-                             const LaunchShape& shape) {
+                             const DeviceStep& d, int32_t* flag, const int32_t* skip,
+                             hipStream_t stream, const LaunchShape& shape) {
   switch (out) {
-    case kOutBf16: return launch_update_flag<R, FP16, kOutBf16>(ts, count, s, flag, skip, stream, shape);
-    case kOutFp16: return launch_update_flag<R, FP16, kOutFp16>(ts, count, s, flag, skip, stream, shape);
-    case kOutNone: return launch_update_flag<R, FP16, kOutNone>(ts, count, s, flag, skip, stream, shape);
+    case kOutBf16: return launch_update_flag<R, FP16, kOutBf16>(ts, count, s, d, flag, skip, stream, shape);
+    case kOutFp16: return launch_update_flag<R, FP16, kOutFp16>(ts, count, s, d, flag, skip, stream, shape);
+    case kOutNone: return launch_update_flag<R, FP16, kOutNone>(ts, count, s, d, flag, skip, stream, shape);
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int R>
 hipError_t launch_update_r(const TensorArgs* ts, int count, bool fp16, int out,
-                           const Scalars& s, int32_t* flag, const int32_t* skip,
-                           hipStream_t stream, const LaunchShape& shape) {
-  return fp16 ? launch_update_out<R, true>(ts, count, out, s, flag, skip, stream, shape)
-              : launch_update_out<R, false>(ts, count, out, s, flag, skip, stream, shape);
+                           const Scalars& s, const DeviceStep& d, int32_t* flag,
+                           const int32_t* skip, hipStream_t stream, const LaunchShape& shape) {
+  return fp16 ? launch_update_out<R, true>(ts, count, out, s, d, flag, skip, stream, shape)
+              : launch_update_out<R, false>(ts, count, out, s, d, flag, skip, stream, shape);
 }
 
 template <int R>
@@ -484,17 +497,15 @@ hipError_t launch_check_r(const TensorArgs* ts, int count, bool fp16, float u, i
 
 }  // namespace
 
-int64_t chunk_elements() { return kChunk < kCheckChunk ? kChunk : kCheckChunk; }
-
 hipError_t launch_layer_adam(const TensorArgs* tensors, int count, int replicas, bool fp16,
-                             int out_dtype, const Scalars& s, int32_t* flag,
-                             const int32_t* skip, hipStream_t stream,
+                             int out_dtype, const Scalars& s, const DeviceStep& dstep,
+                             int32_t* flag, const int32_t* skip, hipStream_t stream,
                              const LaunchShape& shape) {
   switch (replicas) {
-#define LA_CASE(RR)                                                                      \
-  case RR:                                                                               \
-    return launch_update_r<RR>(tensors, count, fp16, out_dtype, s, flag, skip, stream, \
-                               shape);
+#define LA_CASE(RR)                                                                        \
+  case RR:                                                                                 \
+    return launch_update_r<RR>(tensors, count, fp16, out_dtype, s, dstep, flag, skip,    \
+                               stream, shape);
     LA_CASE(1) LA_CASE(2) LA_CASE(3) LA_CASE(4) LA_CASE(5) LA_CASE(6) LA_CASE(7) LA_CASE(8)
 #undef LA_CASE
     default: return hipErrorInvalidValue;

@@ -320,3 +320,22 @@ def test_error_messages_are_per_thread():
         rc, msg = next(iter(msgs))
         assert rc == 1
         assert msg.startswith("num_replicas" if k % 2 == 0 else "step"), msg
+
+
+@host_only
+@pytest.mark.parametrize("case", ["null", "misaligned", "on_master"])
+def test_bad_device_step_pointer(case):
+    t = fake_tensor(0)
+    step = {"null": 0, "misaligned": BASE + 0x50000004, "on_master": t["master"] + 64}[case]
+    desc, keep = la.make_layer([t], 2, la.GRAD_BF16)
+    with pytest.raises(la.LayerAdamError) as e:
+        la.step_device_step_raw(desc, la.make_params(**HP), step)
+    assert e.value.status == {"null": 1, "misaligned": 2, "on_master": 3}[case]
+
+
+@host_only
+def test_device_step_still_checks_the_other_hyperparameters():
+    desc, keep = la.make_layer([fake_tensor(0)], 2, la.GRAD_BF16)
+    with pytest.raises(la.LayerAdamError) as e:
+        la.step_device_step_raw(desc, la.make_params(**dict(HP, beta2=1.5)), BASE + 0x50000000)
+    assert e.value.status == 1

@@ -43,3 +43,57 @@ def test_graph_replays_equal_repeated_oracle_steps():
         assert rep.max_ulp == 0 and gl.flag.item() == 0
         log(f"  replay {replay}: {rep}")
     gl.free()
+
+
+def test_device_step_count_eager_and_at_zero():
+    w = synth.Workload(name="dstep", seed=5100, tensors=(("a", 5), ("b", 4099), ("c", 30001)),
+                       replicas=2, grad_dtype="bf16", step=11)
+    log("case device step eager")
+    L = synth.make_layer(w)
+    gl = GpuLayer(L)
+    t_dev = torch.zeros(1, dtype=torch.int64, device="cuda")
+    before = gl.download()
+    la.step_device_step(gl.params, gl.grads, t_dev, **w.hyper)   # t = 0: no-op
+    after_zero = gl.download()
+    for f in ("master", "exp_avg", "exp_avg_sq", "weight_out"):
+        for a, b in zip(before[f], after_zero[f]):
+            assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), f
+    t_dev.fill_(w.step)
+    la.step_device_step(gl.params, gl.grads, t_dev, **w.hyper)
+    ts = oracle_tensors(L)
+    oracle_step(L, ts)
+    log(f"  {compare(gl.download(), ts, label='dstep')}")
+    gl.free()
+
+
+def test_graph_with_a_device_step_counter_advances_t_every_replay():
+    w = synth.Workload(name="dstep_graph", seed=5200,
+                       tensors=(("a", 3), ("b", 2049), ("c", 70001)),
+                       replicas=4, grad_dtype="fp16", step=1, m_std=None, v_high=None,
+                       grad_prescale=1024.0, unscale=1 / 1024, with_flag=True)
+    log("case graph with device step")
+    L = synth.make_layer(w)
+    gl = GpuLayer(L, out="fp16")
+    t_dev = torch.ones(1, dtype=torch.int64, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    kw = dict(w.hyper, grad_unscale=w.unscale, overflow_flag=gl.flag)
+    with torch.cuda.stream(side):          # warm-up outside capture, t = 1
+        la.step_device_step(gl.params, gl.grads, t_dev, **kw)
+        t_dev.add_(1)
+    side.synchronize()
+    ts = oracle_tensors(L)
+    oracle_step(L, ts, t=1, out="fp16")
+    compare(gl.download(), ts, label="t=1", out="fp16")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        la.step_device_step(gl.params, gl.grads, t_dev, **kw)
+        t_dev.add_(1)
+    for t in range(2, 7):
+        graph.replay()
+        torch.cuda.synchronize()
+        oracle_step(L, ts, t=t, out="fp16")
+        rep = compare(gl.download(), ts, label=f"t={t}", out="fp16")
+        log(f"  replay t={t}: {rep}")
+    assert int(t_dev.item()) == 7 and gl.flag.item() == 0
+    gl.free()
