@@ -136,7 +136,7 @@ typedef struct {
  * is +-Inf or NaN. The library never clears it: the caller zeroes it, may
  * share it across the layers of a step, and reads it after synchronising.
  * The update is applied either way; non-finite values propagate by IEEE
- * rules into m, v, master and the BF16 copy.
+ * rules into m, v, master and the compute copy.
  *
  * Returns LA_OK once the work is enqueued. Every argument is checked on the
  * host before anything is enqueued; on any other status nothing is enqueued

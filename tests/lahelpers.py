@@ -2,7 +2,7 @@
 through the C ABI, run the oracle on the same inputs, compare.
 
 Comparison rule: master, m and v within 2 FP32 ulp (ordered-integer distance,
-+0 and -0 equal, NaN only against NaN); the BF16 copy bit-exact, both against
++0 and -0 equal, NaN only against NaN); the compute copy bit-exact, both against
 the oracle's RNE cast of the GPU's own master and against the oracle's BF16.
 """
 from __future__ import annotations

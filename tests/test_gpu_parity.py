@@ -1,7 +1,7 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle, on MI355X.
 
 Bar: master, m, v within 2 FP32 ulp of the oracle (the sequence of FP32
-operations is the same on both sides, so 0 ulp is expected); the BF16 copy
+operations is the same on both sides, so 0 ulp is expected); the compute copy
 bit-exact; the overflow flag equal. Every input comes from the seeded
 generator (synth) or is written out here; nothing is taken from the GPU side.
 """
