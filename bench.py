@@ -279,6 +279,23 @@ def extras(torch, la, w, params, grads, t0):
     ms = time_launches(torch, lambda: la.step(no_copy, grads, **hp()))
     out["no_compute_copy"] = {"ms": ms, "bytes_per_param": 2 * w.replicas + 24,
                               "gbs": (2 * w.replicas + 24) * n / ms / 1e6}
+    # Host cost of one call (the GPU work stays the same): the functional form
+    # rebuilds the layer descriptor from the tensors each time, a Layer object
+    # describes it once. Measured as host wall time of enqueuing 20 steps.
+    def host_us(fn, reps=20):
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        host = (time.perf_counter() - t_start) / reps * 1e6
+        torch.cuda.synchronize()
+        return host
+
+    layer = la.Layer(params, grads)
+    out["host_us_per_call"] = {
+        "functional": host_us(lambda: la.step(params, grads, **hp())),
+        "layer_object": host_us(lambda: layer.step(**hp())),
+        "tensors": len(params)}
     # Host-resident state: master, m, v in pinned host memory; gradients and
     # the compute copy stay in HBM. 24 B/param cross the host link.
     host = []

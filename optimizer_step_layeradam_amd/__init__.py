@@ -423,6 +423,57 @@ def check_gradients(grads, found_nonfinite, *, grad_unscale: float = 1.0, stream
     del keep
 
 
+class Layer:
+    """A layer's buffers described once: every call then passes only the
+    hyperparameters and flags (the library still checks all arguments on
+    each call). Holds references to the tensors, so they outlive it."""
+
+    def __init__(self, params, grads):
+        self._tensors = (list(params), [list(g) for g in grads])
+        tensors, self.num_replicas, self.grad_dtype, self.out_dtype = _describe(params, grads)
+        self._desc, self._keep = make_layer(tensors, self.num_replicas, self.grad_dtype,
+                                            self.out_dtype)
+        self.numel = sum(t["numel"] for t in tensors)
+
+    def step(self, *, lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
+             step: int, grad_unscale: float = 1.0, overflow_flag=None, stream=None) -> None:
+        step_raw(self._desc, make_params(lr, beta1, beta2, eps, weight_decay, step, grad_unscale),
+                 _flag_ptr(overflow_flag), _stream_ptr(stream))
+
+    def step_range(self, begin: int, end: int, *, lr: float, beta1: float, beta2: float,
+                   eps: float, weight_decay: float, step: int, grad_unscale: float = 1.0,
+                   overflow_flag=None, stream=None) -> None:
+        step_range_raw(self._desc,
+                       make_params(lr, beta1, beta2, eps, weight_decay, step, grad_unscale),
+                       begin, end, _flag_ptr(overflow_flag), _stream_ptr(stream))
+
+    def step_gated(self, skip_if_nonzero, *, lr: float, beta1: float, beta2: float, eps: float,
+                   weight_decay: float, step: int, grad_unscale: float = 1.0,
+                   overflow_flag=None, stream=None) -> None:
+        step_gated_raw(self._desc,
+                       make_params(lr, beta1, beta2, eps, weight_decay, step, grad_unscale),
+                       _flag_ptr(skip_if_nonzero), _flag_ptr(overflow_flag), _stream_ptr(stream))
+
+    def step_device_step(self, step_on_device, *, lr: float, beta1: float, beta2: float,
+                         eps: float, weight_decay: float, grad_unscale: float = 1.0,
+                         overflow_flag=None, stream=None) -> None:
+        step_device_step_raw(self._desc,
+                             make_params(lr, beta1, beta2, eps, weight_decay, 1, grad_unscale),
+                             device_address(step_on_device), _flag_ptr(overflow_flag),
+                             _stream_ptr(stream))
+
+    def check_gradients(self, found_nonfinite, *, grad_unscale: float = 1.0,
+                        stream=None) -> None:
+        check_gradients_raw(self._desc, grad_unscale, _flag_ptr(found_nonfinite),
+                            _stream_ptr(stream))
+
+    def state_bytes(self) -> int:
+        return state_bytes_raw(self._desc)
+
+    def traffic_bytes(self) -> int:
+        return traffic_bytes_raw(self._desc)
+
+
 def state_bytes(numels: Sequence[int], num_replicas: int = 1) -> int:
     """16 bytes per parameter (la_state_bytes)."""
     desc, keep = make_layer([dict(numel=n) for n in numels], num_replicas, GRAD_BF16)

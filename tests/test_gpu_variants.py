@@ -235,3 +235,25 @@ def test_check_then_gated_steps_over_two_layers_without_host_sync():
             for x, y in zip(a[f], b[f]):
                 assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), f
         gl.free()
+
+
+def test_layer_object_matches_the_functional_calls():
+    w = ragged(3, with_flag=True)
+    L = synth.make_layer(w)
+    a, b = GpuLayer(L), GpuLayer(L)
+    layer = la.Layer(b.params, b.grads)
+    assert layer.numel == w.numel and layer.traffic_bytes() == w.traffic_bytes
+    for t in (5, 6):
+        la.step(a.params, a.grads, step=t, overflow_flag=a.flag, **w.hyper)
+        layer.step(step=t, overflow_flag=b.flag, **w.hyper)
+    la.step_range(a.params, a.grads, 10, 70000, step=7, **w.hyper)
+    layer.step_range(10, 70000, step=7, **w.hyper)
+    ga, gb = a.download(), b.download()
+    for f in ("master", "exp_avg", "exp_avg_sq", "weight_out"):
+        for x, y in zip(ga[f], gb[f]):
+            assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), f
+    found = torch.zeros(1, dtype=torch.int32, device="cuda")
+    layer.check_gradients(found)
+    assert int(found.item()) == 0
+    a.free()
+    b.free()
