@@ -21,16 +21,19 @@
 // dispatcher then keeps the workgroups in flight on a narrow, advancing
 // window of every stream, which measured faster on MI355X than a
 // persistent grid whose workgroups drift apart (the loop below still
-// strides by the grid when the grid is capped). The launch also reserves
-// LDS that the kernel never touches, so that a compute unit holds only two
-// workgroups (four waves, one per SIMD) at a time: fewer requests in flight
-// interleave the 2R + 8 streams less at the HBM, and that measured fastest.
-// A chunk is U tiles of 128 threads x 4 elements: each thread owns 4
-// consecutive elements per tile and a wave's U tiles are adjacent, so a wave
-// reads U KiB runs of each FP32 stream (16 B per lane) and U/2 KiB runs of
-// each 16-bit gradient stream (8 B per lane). A thread issues every load of
-// its U tiles before any arithmetic, (12 + 2R) * 4 * U bytes per lane in
-// flight. Every access carries the non-temporal hint: nothing is reused.
+// strides by the grid when the grid is capped). A workgroup is one wave of
+// 64 lanes and a chunk two tiles of 64 x 4 elements: each lane owns 4
+// consecutive elements per tile and the two tiles are adjacent, so a wave
+// reads 2 KiB runs of each FP32 stream (16 B per lane) and 1 KiB runs of
+// each 16-bit gradient stream (8 B per lane), and a lane issues every load
+// of both tiles before any arithmetic, (12 + 2R) * 8 bytes in flight. The
+// launch also reserves LDS that the kernel never touches, so that a compute
+// unit holds only a few of these waves at a time: 7 for R <= 4 replicas, 6
+// above. Fewer requests in flight interleave the 2R + 8 streams less at the
+// HBM; on the 14B-shaped layer this shape and these residencies measured
+// fastest at every R from 1 to 8 (against wider workgroups, more tiles per
+// chunk and other residencies). Every access carries the non-temporal hint:
+// nothing is reused.
 //
 // Arithmetic is IEEE binary32 with one rounding per operation: contraction
 // into fused multiply-adds is switched off for this file, and division and
@@ -46,18 +49,17 @@
 namespace la {
 namespace {
 
-// Tile shape and cache hints. The defaults are the measured best on MI355X
-// for the Qwen3-14B-shaped layer at R = 8 (and within a few per cent of the
-// best on the other layer shapes measured); the macros exist so that other
-// shapes can be built and compared.
+// Tile shape, residency and cache hints. The defaults are the measured best
+// on MI355X for the Qwen3-14B-shaped layer at R = 1..8; the macros exist so
+// that other shapes can be built and compared.
 #ifndef LA_BLOCK
-#define LA_BLOCK 128
+#define LA_BLOCK 64
 #endif
 #ifndef LA_TILE_VEC
 #define LA_TILE_VEC 4
 #endif
 #ifndef LA_TILE_UNROLL
-#define LA_TILE_UNROLL 4
+#define LA_TILE_UNROLL 2
 #endif
 #ifndef LA_NT_LOADS
 #define LA_NT_LOADS 1
@@ -68,12 +70,23 @@ namespace {
 #ifndef LA_WAVE_CONTIG
 #define LA_WAVE_CONTIG 1   // 1: each wave's tiles are adjacent in memory
 #endif
+// Update: resident workgroups per compute unit (0: no cap), for R up to
+// LA_FEW_REPLICAS and for more replicas.
+#ifndef LA_FEW_REPLICAS
+#define LA_FEW_REPLICAS 4
+#endif
+#ifndef LA_WORKGROUPS_PER_CU_FEW_REPLICAS
+#define LA_WORKGROUPS_PER_CU_FEW_REPLICAS 7
+#endif
 #ifndef LA_WORKGROUPS_PER_CU
-#define LA_WORKGROUPS_PER_CU 2  // update: resident workgroups per compute unit (0: no cap)
+#define LA_WORKGROUPS_PER_CU 6
 #endif
 // The finite check only reads: more requests in flight help it (measured
-// 7.1 TB/s with 8 tiles per chunk and no residency cap, against 5.5 TB/s
-// with the update's shape).
+// 7.1 TB/s with 128-thread workgroups, 8 tiles per chunk and no residency
+// cap, against 5.5 TB/s with a residency cap of one wave per SIMD).
+#ifndef LA_CHECK_BLOCK
+#define LA_CHECK_BLOCK 128      // finite check: threads per workgroup
+#endif
 #ifndef LA_CHECK_TILE_UNROLL
 #define LA_CHECK_TILE_UNROLL 8  // finite check: tiles per chunk
 #endif
@@ -86,12 +99,19 @@ constexpr int kVec = LA_TILE_VEC;       // consecutive elements per thread per t
 constexpr int kUnroll = LA_TILE_UNROLL; // tiles per chunk
 constexpr int kChunk = kBlock * kVec * kUnroll;
 constexpr int kQuads = kVec / 4;        // 16-byte FP32 vectors per array per tile
+constexpr int kCheckBlock = LA_CHECK_BLOCK;
 constexpr int kCheckUnroll = LA_CHECK_TILE_UNROLL;
-constexpr int kCheckChunk = kBlock * kVec * kCheckUnroll;
+constexpr int kCheckChunk = kCheckBlock * kVec * kCheckUnroll;
 static_assert(kVec == 4 || kVec == 8, "4 or 8 elements per thread per tile");
 static_assert(kBlock % 64 == 0 && kBlock <= 1024, "whole waves");
+static_assert(kCheckBlock % 64 == 0 && kCheckBlock <= 1024, "whole waves");
 static_assert(kChunk > kMaxUnalignedEntry && kCheckChunk > kMaxUnalignedEntry,
               "short unaligned entries must take the element-wise path");
+
+template <int R>
+constexpr int update_workgroups_per_cu() {
+  return R <= LA_FEW_REPLICAS ? LA_WORKGROUPS_PER_CU_FEW_REPLICAS : LA_WORKGROUPS_PER_CU;
+}
 
 // Native vector types (the non-temporal builtins need them).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -217,15 +237,16 @@ __device__ __forceinline__ float aggregate_one(const uint16_t* const (&g)[R], in
   return x * u;
 }
 
-// Element offset, within its chunk of TILES tiles, of thread tid's first
-// element in tile u. Tile-major: tile u covers [u, u + 1) * kBlock * kVec.
-// Wave-contiguous: wave w owns TILES adjacent runs of 64 * kVec elements.
-template <int TILES = kUnroll>
+// Element offset, within its chunk of TILES tiles of BLOCK threads, of
+// thread tid's first element in tile u. Tile-major: tile u covers
+// [u, u + 1) * BLOCK * kVec. Wave-contiguous: wave w owns TILES adjacent runs
+// of 64 * kVec elements.
+template <int BLOCK, int TILES>
 __device__ __forceinline__ uint32_t tile_offset(int u, int tid) {
   if constexpr (LA_WAVE_CONTIG) {
     return static_cast<uint32_t>((((tid >> 6) * TILES + u) * 64 + (tid & 63)) * kVec);
   } else {
-    return static_cast<uint32_t>((u * kBlock + tid) * kVec);
+    return static_cast<uint32_t>((u * BLOCK + tid) * kVec);
   }
 }
 
@@ -302,7 +323,7 @@ layer_adam_kernel(const KernelArgs<R> a) {
       half_words G[kUnroll][R];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        const uint32_t off = tile_offset(u, tid);
+        const uint32_t off = tile_offset<kBlock, kUnroll>(u, tid);
 #pragma unroll
         for (int q = 0; q < kQuads; ++q) {
           P[u][q] = load_stream(reinterpret_cast<const f32x4*>(p + off) + q);
@@ -322,7 +343,7 @@ layer_adam_kernel(const KernelArgs<R> a) {
           if (FLAG) bad |= !__builtin_isfinite(gk);
           e[k] = adam_update(gk, P[u][k / 4][k % 4], M[u][k / 4][k % 4], V[u][k / 4][k % 4], s);
         }
-        store_tile<OUT>(e, p, m, v, w, tile_offset(u, tid));
+        store_tile<OUT>(e, p, m, v, w, tile_offset<kBlock, kUnroll>(u, tid));
       }
     } else {
       // Last, partial chunk of a tensor: element by element, bounds-checked.
@@ -354,7 +375,7 @@ layer_adam_kernel(const KernelArgs<R> a) {
 
 // ---- the finite-check pre-pass -------------------------------------------------
 template <int R, bool FP16>
-__global__ void __launch_bounds__(kBlock)
+__global__ void __launch_bounds__(kCheckBlock)
 check_kernel(const KernelArgs<R> a) {
   // Already found (by an earlier layer or by other workgroups of this launch,
   // hence the atomic read): the answer cannot change.
@@ -379,7 +400,7 @@ check_kernel(const KernelArgs<R> a) {
       half_words G[kCheckUnroll][R];
 #pragma unroll
       for (int tile = 0; tile < kCheckUnroll; ++tile) {
-        const uint32_t off = tile_offset<kCheckUnroll>(tile, tid);
+        const uint32_t off = tile_offset<kCheckBlock, kCheckUnroll>(tile, tid);
 #pragma unroll
         for (int r = 0; r < R; ++r)
           G[tile][r] = load_stream(reinterpret_cast<const half_words*>(g[r] + off));
@@ -395,7 +416,7 @@ check_kernel(const KernelArgs<R> a) {
       for (int tile = 0; tile < kCheckUnroll; ++tile) {
 #pragma unroll
         for (int k = 0; k < kVec; ++k) {
-          const int64_t i = static_cast<int64_t>((tile * kBlock + tid) * kVec + k);
+          const int64_t i = static_cast<int64_t>((tile * kCheckBlock + tid) * kVec + k);
           if (i < left) bad |= !__builtin_isfinite(aggregate_one<R, FP16>(g, i, u));
         }
       }
@@ -432,11 +453,11 @@ int lds_reservation(const LaunchShape& shape, int default_per_cu) {
   return bytes <= shape.lds_per_block ? bytes : 0;
 }
 
-hipError_t launch(const void* kernel, void* args, int64_t chunks, int lds, hipStream_t stream,
-                  const LaunchShape& shape) {
+hipError_t launch(const void* kernel, void* args, int64_t chunks, int block, int lds,
+                  hipStream_t stream, const LaunchShape& shape) {
   const int64_t grid = chunks < shape.grid_cap ? chunks : shape.grid_cap;  // >= 1
   void* params[] = {args};
-  return hipLaunchKernel(kernel, dim3(static_cast<unsigned>(grid)), dim3(kBlock), params,
+  return hipLaunchKernel(kernel, dim3(static_cast<unsigned>(grid)), dim3(block), params,
                          static_cast<unsigned>(lds), stream);
 }
 
@@ -451,7 +472,8 @@ hipError_t launch_update_typed(const TensorArgs* ts, int count, const Scalars& s
   a.flag = flag;
   a.skip = skip;
   return launch(reinterpret_cast<const void*>(&layer_adam_kernel<R, FP16, FLAG, OUT>), &a,
-                chunks, lds_reservation(shape, LA_WORKGROUPS_PER_CU), stream, shape);
+                chunks, kBlock, lds_reservation(shape, update_workgroups_per_cu<R>()), stream,
+                shape);
 }
 
 template <int R, bool FP16, int OUT>
@@ -491,8 +513,8 @@ hipError_t launch_check_r(const TensorArgs* ts, int count, bool fp16, float u, i
   a.flag = flag;
   const void* k = fp16 ? reinterpret_cast<const void*>(&check_kernel<R, true>)
                        : reinterpret_cast<const void*>(&check_kernel<R, false>);
-  return launch(k, &a, chunks, lds_reservation(shape, LA_CHECK_WORKGROUPS_PER_CU), stream,
-                shape);
+  return launch(k, &a, chunks, kCheckBlock, lds_reservation(shape, LA_CHECK_WORKGROUPS_PER_CU),
+                stream, shape);
 }
 
 }  // namespace

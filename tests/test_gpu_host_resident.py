@@ -8,12 +8,10 @@ import torch
 
 import optimizer_step_layeradam_amd as la
 import synth
-from lahelpers import compare, log, oracle_step, oracle_tensors
+from lahelpers import RAGGED, compare, log, oracle_step, oracle_tensors
 
 pytestmark = pytest.mark.gpu
 
-RAGGED = (("a", 1), ("b", 3), ("c", 7), ("d", 2047), ("e", 2048), ("f", 2049),
-          ("g", 4101), ("h", 10001), ("i", 65536 + 13))
 
 
 def pinned(a: np.ndarray) -> torch.Tensor:

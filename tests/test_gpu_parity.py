@@ -12,7 +12,7 @@ import torch
 import optimizer_step_layeradam_amd as la
 import oracle
 import synth
-from lahelpers import (GpuLayer, Report, compare, log, oracle_step, oracle_tensors,
+from lahelpers import (RAGGED, GpuLayer, Report, compare, log, oracle_step, oracle_tensors,
                        sample_indices)
 
 pytestmark = pytest.mark.gpu
@@ -56,8 +56,6 @@ def test_workload_reduced(name):
     assert rep.max_ulp <= 2
 
 
-RAGGED = (("a", 1), ("b", 3), ("c", 7), ("d", 2047), ("e", 2048), ("f", 2049),
-          ("g", 4101), ("h", 10001), ("i", 65536 + 13))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])

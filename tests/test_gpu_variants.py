@@ -8,12 +8,10 @@ import torch
 import optimizer_step_layeradam_amd as la
 import oracle
 import synth
-from lahelpers import GpuLayer, compare, log, oracle_step, oracle_tensors
+from lahelpers import RAGGED, GpuLayer, compare, log, oracle_step, oracle_tensors
 
 pytestmark = pytest.mark.gpu
 
-RAGGED = (("a", 1), ("b", 3), ("c", 7), ("d", 2047), ("e", 2048), ("f", 2049),
-          ("g", 4101), ("h", 10001), ("i", 65536 + 13))
 
 
 def ragged(R, dtype="bf16", seed=3000, **kw):
@@ -145,18 +143,19 @@ def test_gradient_check_matches_the_oracle(dtype, inject):
     w = ragged(4, dtype)
     log(f"case check {dtype} {inject}")
     L = synth.make_layer(w)
+    ix = {name: i for i, (name, _) in enumerate(w.tensors)}
     unscale = 1.0
     codes = {"bf16": (0x7F80, 0xFF80, 0x7FC1, 0x7F7F), "fp16": (0x7C00, 0xFC00, 0x7E01, 0x7BFF)}
     inf, ninf, nan, big = codes[dtype]
     if inject == "inf":
-        L.grad(2, 8)[65536 + 12] = inf        # last element of the last tensor
+        L.grad(2, ix["i"])[65536 + 12] = inf     # last element of the longest tensor
     elif inject == "nan":
-        L.grad(0, 3)[1000] = nan
+        L.grad(0, ix["d"])[1000] = nan
     elif inject == "cancel":
-        L.grad(1, 5)[7], L.grad(3, 5)[7] = inf, ninf
+        L.grad(1, ix["f"])[7], L.grad(3, ix["f"])[7] = inf, ninf
     elif inject == "unscale":
         for r in range(4):
-            L.grad(r, 6)[5] = big
+            L.grad(r, ix["g"])[5] = big
         unscale = 2.0 ** 112 if dtype == "fp16" else 1.0
     gl = GpuLayer(L)
     found = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -218,7 +217,7 @@ def test_check_then_gated_steps_over_two_layers_without_host_sync():
         w = ragged(2, "fp16", seed=3300 + 10 * k, grad_prescale=1024.0, unscale=1 / 1024)
         L = synth.make_layer(w)
         if k == 1:
-            L.grad(0, 7)[123] = 0x7C00   # +Inf in the second layer
+            L.grad(0, [n for n, _ in w.tensors].index("h"))[123] = 0x7C00  # +Inf, 2nd layer
         layers.append((w, L, GpuLayer(L)))
     found = torch.zeros(1, dtype=torch.int32, device="cuda")
     for w, L, gl in layers:
