@@ -219,6 +219,49 @@ def copy_reference(torch, mib: int = 2048, reps: int = 10):
             "kernel": "Tensor.copy_ (device copy)"}
 
 
+def host_link_reference(torch, mib: int = 1024, reps: int = 5):
+    """Bandwidth of the host link for pinned buffers: DMA copies host to
+    device, device to host, and both at once on two streams. An update whose
+    state lives in host memory moves as many bytes each way; its ceiling is
+    the sum of the two one-way rates (a full-duplex link), which the two
+    concurrent copies need not reach."""
+    n = mib << 20
+    h_in = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    h_out = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    d_in = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    d_out = torch.zeros(n, dtype=torch.uint8, device="cuda:0")
+    h_in.fill_(1)
+    up, down = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def wall_ms(fn):
+        fn()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t_start) / reps * 1e3
+
+    def h2d():
+        with torch.cuda.stream(up):
+            d_in.copy_(h_in, non_blocking=True)
+
+    def d2h():
+        with torch.cuda.stream(down):
+            h_out.copy_(d_out, non_blocking=True)
+
+    def both():
+        h2d()
+        d2h()
+
+    out = {"bytes_per_direction": n, "kernel": "Tensor.copy_ (DMA, pinned host)"}
+    for name, fn, moved in (("h2d", h2d, n), ("d2h", d2h, n), ("both", both, 2 * n)):
+        out[f"{name}_gbs"] = moved / wall_ms(fn) / 1e6
+    del h_in, h_out, d_in, d_out
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_launches(torch, fn, reps=10, warm=2):
     """Mean milliseconds of fn() over reps, HIP events on the current stream."""
     for _ in range(warm):
@@ -306,10 +349,14 @@ def extras(torch, la, w, params, grads, t0):
         hv.copy_(v)
         host.append((hp_, hm, hv, wb))
     ms = time_launches(torch, lambda: la.step(host, grads, **hp()), reps=3, warm=1)
+    del host
+    link = host_link_reference(torch)
     out["host_resident_state"] = {"ms": ms, "gparams": n / ms / 1e6,
                                   "host_link_bytes_per_param": 24,
-                                  "host_link_gbs": 24 * n / ms / 1e6}
-    del host
+                                  "host_link_gbs": 24 * n / ms / 1e6,
+                                  "frac_of_dma_h2d_plus_d2h":
+                                      24 * n / ms / 1e6 / (link["h2d_gbs"] + link["d2h_gbs"]),
+                                  "host_link_reference": link}
     return out
 
 
