@@ -389,8 +389,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the multi-GPU sharding of the update is a design note, not code)",
+        print(f"bench.py: the LayerAdam library drives one GPU; --gpus {args.gpus} is not "
+              "supported (sharding the update across GPUs is described, not implemented)",
               file=sys.stderr, flush=True)
         sys.exit(2)
     if args.calibrate_copy_mib:
