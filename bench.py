@@ -281,8 +281,9 @@ def time_launches(torch, fn, reps=10, warm=2):
 def extras(torch, la, w, params, grads, t0):
     """The neighbouring entry points on the same resident layer, timed after
     the main region: the layer released in 64 MiB gradient chunks through the
-    range entry point, the finite-check pre-pass, check + gated step, and the
-    FP16 and no compute copies."""
+    range entry point, the finite-check pre-pass, check + gated step, the
+    FP16 and no compute copies, the host cost of a call, one GPU's shard of
+    the layer split 2, 4 or 8 ways, and the state held in pinned host memory."""
     n = w.numel
     t = [t0]
 
@@ -339,6 +340,16 @@ def extras(torch, la, w, params, grads, t0):
         "functional": host_us(lambda: la.step(params, grads, **hp())),
         "layer_object": host_us(lambda: layer.step(**hp())),
         "tensors": len(params)}
+    # One GPU's share of a layer sharded G ways by element range (each GPU
+    # owning the master, m and v of its range): the middle shard, which
+    # crosses tensor boundaries, updated alone through the range entry point.
+    shards = {}
+    for g in (2, 4, 8):
+        lo, hi = n * (g // 2) // g, n * (g // 2 + 1) // g
+        ms = time_launches(torch, lambda: layer.step_range(lo, hi, **hp()))
+        shards[str(g)] = {"elements": hi - lo, "ms": ms,
+                          "gbs": w.traffic_bytes * (hi - lo) / n / ms / 1e6}
+    out["one_shard_of_g"] = shards
     # Host-resident state: master, m, v in pinned host memory; gradients and
     # the compute copy stay in HBM. 24 B/param cross the host link.
     host = []
