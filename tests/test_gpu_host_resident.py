@@ -13,7 +13,6 @@ from lahelpers import RAGGED, compare, log, oracle_step, oracle_tensors
 pytestmark = pytest.mark.gpu
 
 
-
 def pinned(a: np.ndarray) -> torch.Tensor:
     t = torch.empty(a.shape, dtype=torch.from_numpy(a[:0]).dtype, pin_memory=True)
     t.copy_(torch.from_numpy(a))

@@ -56,8 +56,6 @@ def test_workload_reduced(name):
     assert rep.max_ulp <= 2
 
 
-
-
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("R", range(1, 9))
 def test_every_replica_count_and_dtype(R, dtype):

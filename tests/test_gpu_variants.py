@@ -13,7 +13,6 @@ from lahelpers import RAGGED, GpuLayer, compare, log, oracle_step, oracle_tensor
 pytestmark = pytest.mark.gpu
 
 
-
 def ragged(R, dtype="bf16", seed=3000, **kw):
     return synth.Workload(name=f"ragged_R{R}_{dtype}", seed=seed + R, tensors=RAGGED,
                           replicas=R, grad_dtype=dtype, step=5, **kw)
@@ -256,3 +255,64 @@ def test_layer_object_matches_the_functional_calls():
     assert int(found.item()) == 0
     a.free()
     b.free()
+
+
+def test_concurrent_calls_from_host_threads():
+    """Four host threads update four layers at once, each on its own stream
+    (the binding releases the interpreter lock inside the call), while a
+    fifth thread keeps making a call the library refuses: every layer ends
+    equal to three oracle steps, and each refusal reports its own error."""
+    import threading
+    log("case host threads")
+    layers = []
+    for k in range(4):
+        w = synth.replace(ragged(1 + 2 * k, seed=3400 + 10 * k), step=1, m_std=None,
+                          v_high=None)
+        L = synth.make_layer(w)
+        layers.append((w, L, GpuLayer(L)))
+    streams = [torch.cuda.Stream() for _ in layers]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    barrier = threading.Barrier(len(layers) + 1)
+    failures, refusals = [], []
+
+    def updater(k):
+        w, _, gl = layers[k]
+        layer = la.Layer(gl.params, gl.grads)
+        barrier.wait()
+        try:
+            for t in (1, 2, 3):
+                layer.step(step=t, grad_unscale=w.unscale, stream=streams[k], **w.hyper)
+        except Exception as e:  # reported below, on the main thread
+            failures.append(repr(e))
+
+    def refuser():
+        w, _, gl = layers[0]
+        barrier.wait()
+        for _ in range(200):
+            try:
+                la.step(gl.params, gl.grads, step=0, **w.hyper)  # t = 0 is refused
+                failures.append("step 0 accepted")
+            except la.LayerAdamError as e:
+                refusals.append(str(e))
+            except Exception as e:  # reported below, on the main thread
+                failures.append(repr(e))
+
+    threads = [threading.Thread(target=updater, args=(k,)) for k in range(len(layers))]
+    threads.append(threading.Thread(target=refuser))
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    for s in streams:
+        s.synchronize()
+    assert not failures, failures
+    assert len(refusals) == 200 and all("step = 0" in r for r in refusals), set(refusals)
+    for w, L, gl in layers:
+        ts = oracle_tensors(L)
+        for t in (1, 2, 3):
+            oracle_step(L, ts, t=t)
+        rep = compare(gl.download(), ts, label=w.name)
+        log(f"  {rep}")
+        assert rep.max_ulp == 0
+        gl.free()
