@@ -1,0 +1,52 @@
+"""bench.py end to end on MI355X, in a child process: one JSON line with the
+fields its readers rely on, self-consistent, and a CPU baseline that agrees
+with the GPU's first step."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_prints_one_consistent_json_line():
+    print("case bench.py --steps 3 --warmup 1 --no-extras --cpu-seconds 1", flush=True)
+    r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--steps", "3",
+                        "--warmup", "1", "--no-extras", "--cpu-seconds", "1"],
+                       capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [x for x in r.stdout.splitlines() if x.strip()]
+    assert len(lines) == 1, r.stdout[-2000:]
+    d = json.loads(lines[0])
+    w = synth.WORKLOADS[synth.BENCH_WORKLOAD]
+
+    assert d["unit"] == "Gparam/s" and d["higher_is_better"] is True
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
+    assert d["data"] == "synthetic" and d["dtype"] == "f32" and d["vs_baseline"] is None
+    assert d["config"]["workload"] == w.name and d["config"]["params"] == w.numel
+    assert d["config"]["replicas"] == w.replicas
+    # value is the parameters updated per second over the timed region
+    assert d["value"] == pytest.approx(w.numel / (d["ms_per_step"] / 1e3) / 1e9, rel=1e-9)
+
+    rf = d["roofline"]
+    assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
+    assert rf["algorithmic_bytes_per_launch"] == w.traffic_bytes == \
+        (2 * w.replicas + 26) * w.numel
+    assert rf["achieved"] == pytest.approx(
+        w.traffic_bytes / (rf["mean_launch_ms"] / 1e3) / 1e9, rel=1e-9)
+    assert rf["frac"] == pytest.approx(rf["achieved"] / rf["peak"], rel=1e-12)
+    assert 0.0 < rf["frac"] < 1.0
+    assert rf["min_launch_ms"] <= rf["mean_launch_ms"] <= rf["max_launch_ms"]
+    assert rf["traffic"] is None or rf["traffic"] > 0
+
+    cb = d["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["cores"] == 1 and cb["value"] > 0
+    assert cb["unit"] == "Gparam/s" and cb["sample"]
+    par = cb["parity_vs_gpu_first_step"]
+    assert par["params"] > 0 and par["max_ulp"] <= 2 and par["bf16_mismatch"] == 0
