@@ -29,11 +29,12 @@
 // of both tiles before any arithmetic, (12 + 2R) * 8 bytes in flight. The
 // launch also reserves LDS that the kernel never touches, so that a compute
 // unit holds only a few of these waves at a time: 7 for R <= 4 replicas, 6
-// above. Fewer requests in flight interleave the 2R + 8 streams less at the
-// HBM; on the 14B-shaped layer this shape and these residencies measured
-// fastest at every R from 1 to 8 (against wider workgroups, more tiles per
-// chunk and other residencies). Every access carries the non-temporal hint:
-// nothing is reused.
+// above. Fewer requests in flight interleave the R + 7 streams (R gradient
+// reads; master, m, v read and written; the compute copy) less at the HBM;
+// on the 14B-shaped layer this shape and these residencies measured fastest
+// at every R from 1 to 8 (against wider workgroups, more tiles per chunk and
+// other residencies). Every access carries the non-temporal hint: nothing
+// is reused.
 //
 // Arithmetic is IEEE binary32 with one rounding per operation: contraction
 // into fused multiply-adds is switched off for this file, and division and
