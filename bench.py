@@ -425,9 +425,13 @@ def main():
     flag = torch.zeros(1, dtype=torch.int32, device="cuda:0") if w.with_flag else None
     stream = torch.cuda.current_stream()
 
+    # The layer is described once; every step then passes only t (the
+    # library still checks every argument on each call).
+    layer = la.Layer(params, grads)
+
     def one_step(t):
-        la.step(params, grads, step=t, grad_unscale=w.unscale, overflow_flag=flag,
-                stream=stream, **w.hyper)
+        layer.step(step=t, grad_unscale=w.unscale, overflow_flag=flag, stream=stream,
+                   **w.hyper)
 
     # first step on the fresh inputs: its outputs feed the CPU-baseline parity
     one_step(w.step)
