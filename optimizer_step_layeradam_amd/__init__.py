@@ -300,6 +300,8 @@ def _describe(params, grads, need_state: bool = True):
     if not grads:
         return [], 1, GRAD_BF16, OUT_BF16
     R = len(grads[0])
+    if R > MAX_REPLICAS:
+        raise ValueError(f"{R} gradient replicas per tensor; at most {MAX_REPLICAS}")
     gd = _grad_dtype_of(grads)
     od = _out_dtype_of(params) if need_state else OUT_NONE
     out = []
@@ -334,13 +336,24 @@ def _describe(params, grads, need_state: bool = True):
     return out, R, gd, od
 
 
-def _flag_ptr(flag) -> int:
+def _scalar_ptr(t, dtype, what: str) -> int:
+    """Address of a one-element (or longer) device scalar of ``dtype`` on the
+    current device: the library reads or writes its first element."""
+    if not t.is_cuda or t.dtype != dtype:
+        raise TypeError(f"{what} must be a {dtype} CUDA tensor, got {t.dtype} on {t.device}")
+    if t.numel() < 1:
+        raise ValueError(f"{what} has no elements")
+    return device_address(t)
+
+
+def _flag_ptr(flag, what: str = "the flag") -> int:
     import torch
-    if flag is None:
-        return 0
-    if flag.dtype != torch.int32 or not flag.is_cuda:
-        raise TypeError("flags must be int32 CUDA tensors")
-    return flag.data_ptr()
+    return 0 if flag is None else _scalar_ptr(flag, torch.int32, what)
+
+
+def _step_ptr(step_on_device) -> int:
+    import torch
+    return _scalar_ptr(step_on_device, torch.int64, "step_on_device")
 
 
 def _stream_ptr(stream) -> int:
@@ -391,8 +404,8 @@ def step_gated(params, grads, skip_if_nonzero, *, lr: float, beta1: float, beta2
     tensors, R, gd, od = _describe(params, grads)
     desc, keep = make_layer(tensors, R, gd, od)
     hp = make_params(lr, beta1, beta2, eps, weight_decay, step, grad_unscale)
-    step_gated_raw(desc, hp, _flag_ptr(skip_if_nonzero), _flag_ptr(overflow_flag),
-                   _stream_ptr(stream))
+    step_gated_raw(desc, hp, _flag_ptr(skip_if_nonzero, "skip_if_nonzero"),
+                   _flag_ptr(overflow_flag), _stream_ptr(stream))
     del keep
 
 
@@ -402,14 +415,11 @@ def step_device_step(params, grads, step_on_device, *, lr: float, beta1: float, 
     """The update with t read on the GPU from the int64 CUDA scalar
     ``step_on_device`` when the kernel runs (graph-capturable: advance the
     counter on the device between replays)."""
-    import torch
-    if step_on_device.dtype != torch.int64 or not step_on_device.is_cuda:
-        raise TypeError("step_on_device must be an int64 CUDA tensor")
+    t_ptr = _step_ptr(step_on_device)
     tensors, R, gd, od = _describe(params, grads)
     desc, keep = make_layer(tensors, R, gd, od)
     hp = make_params(lr, beta1, beta2, eps, weight_decay, 1, grad_unscale)
-    step_device_step_raw(desc, hp, device_address(step_on_device), _flag_ptr(overflow_flag),
-                         _stream_ptr(stream))
+    step_device_step_raw(desc, hp, t_ptr, _flag_ptr(overflow_flag), _stream_ptr(stream))
     del keep
 
 
@@ -419,7 +429,8 @@ def check_gradients(grads, found_nonfinite, *, grad_unscale: float = 1.0, stream
     grads: per tensor a list of R replicas."""
     tensors, R, gd, _ = _describe([None] * len(grads), grads, need_state=False)
     desc, keep = make_layer(tensors, R, gd, OUT_NONE)
-    check_gradients_raw(desc, grad_unscale, _flag_ptr(found_nonfinite), _stream_ptr(stream))
+    check_gradients_raw(desc, grad_unscale, _flag_ptr(found_nonfinite, "found_nonfinite"),
+                        _stream_ptr(stream))
     del keep
 
 
@@ -452,20 +463,21 @@ class Layer:
                    overflow_flag=None, stream=None) -> None:
         step_gated_raw(self._desc,
                        make_params(lr, beta1, beta2, eps, weight_decay, step, grad_unscale),
-                       _flag_ptr(skip_if_nonzero), _flag_ptr(overflow_flag), _stream_ptr(stream))
+                       _flag_ptr(skip_if_nonzero, "skip_if_nonzero"), _flag_ptr(overflow_flag),
+                       _stream_ptr(stream))
 
     def step_device_step(self, step_on_device, *, lr: float, beta1: float, beta2: float,
                          eps: float, weight_decay: float, grad_unscale: float = 1.0,
                          overflow_flag=None, stream=None) -> None:
         step_device_step_raw(self._desc,
                              make_params(lr, beta1, beta2, eps, weight_decay, 1, grad_unscale),
-                             device_address(step_on_device), _flag_ptr(overflow_flag),
+                             _step_ptr(step_on_device), _flag_ptr(overflow_flag),
                              _stream_ptr(stream))
 
     def check_gradients(self, found_nonfinite, *, grad_unscale: float = 1.0,
                         stream=None) -> None:
-        check_gradients_raw(self._desc, grad_unscale, _flag_ptr(found_nonfinite),
-                            _stream_ptr(stream))
+        check_gradients_raw(self._desc, grad_unscale,
+                            _flag_ptr(found_nonfinite, "found_nonfinite"), _stream_ptr(stream))
 
     def state_bytes(self) -> int:
         return state_bytes_raw(self._desc)

@@ -339,3 +339,21 @@ def test_device_step_still_checks_the_other_hyperparameters():
     with pytest.raises(la.LayerAdamError) as e:
         la.step_device_step_raw(desc, la.make_params(**dict(HP, beta2=1.5)), BASE + 0x50000000)
     assert e.value.status == 1
+
+
+def test_binding_refuses_host_flags_and_step_counts_before_any_call():
+    """Flags and the device step count must be device scalars of the right
+    type; a host tensor is refused in the binding, before the library runs."""
+    import torch
+    with pytest.raises(TypeError):
+        la._flag_ptr(torch.zeros(1, dtype=torch.int32))
+    with pytest.raises(TypeError):
+        la._step_ptr(torch.ones(1, dtype=torch.int64))
+
+
+def test_binding_refuses_more_than_eight_replicas():
+    import torch
+    p = torch.zeros(8)
+    grads = [[torch.zeros(8, dtype=torch.bfloat16)] * (la.MAX_REPLICAS + 1)]
+    with pytest.raises(ValueError, match="at most 8"):
+        la._describe([(p, p, p, None)], grads)

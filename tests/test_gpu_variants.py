@@ -316,3 +316,36 @@ def test_concurrent_calls_from_host_threads():
         log(f"  {rep}")
         assert rep.max_ulp == 0
         gl.free()
+
+
+def test_binding_refuses_bad_device_scalars_without_launching():
+    """A device step count that is not int64, and flags that are not int32 or
+    have no element, are refused before anything is enqueued: the layer's
+    state is unchanged afterwards."""
+    log("case bad device scalars")
+    w = ragged(2)
+    L = synth.make_layer(w)
+    gl = GpuLayer(L)
+    layer = la.Layer(gl.params, gl.grads)
+    before = gl.download()
+    hp = dict(w.hyper)
+    int32_step = torch.ones(1, dtype=torch.int32, device="cuda")  # 4 bytes, not 8
+    empty_flag = torch.zeros(0, dtype=torch.int32, device="cuda")
+    float_flag = torch.zeros(1, dtype=torch.float32, device="cuda")
+    with pytest.raises(TypeError):
+        layer.step_device_step(int32_step, **hp)
+    with pytest.raises(TypeError):
+        la.step_device_step(gl.params, gl.grads, int32_step, **hp)
+    with pytest.raises(ValueError):
+        layer.step(step=3, overflow_flag=empty_flag, **hp)
+    with pytest.raises(TypeError):
+        layer.step(step=3, overflow_flag=float_flag, **hp)
+    with pytest.raises(ValueError):
+        layer.step_gated(empty_flag, step=3, **hp)
+    with pytest.raises(ValueError):
+        layer.check_gradients(empty_flag)
+    after = gl.download()
+    for f in ("master", "exp_avg", "exp_avg_sq", "weight_out"):
+        for x, y in zip(before[f], after[f]):
+            assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), f
+    gl.free()
