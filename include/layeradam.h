@@ -49,8 +49,9 @@
  * call returns. Calls are asynchronous on the given stream; buffers must
  * stay alive until the stream reaches the work.
  *
- * Thread safety: no global mutable state apart from a thread-local error
- * message and a per-device cache of the compute-unit count.
+ * Thread safety: calls may come from several host threads at once. The only
+ * global state is a thread-local error message and, per device, the LDS
+ * sizes the launch shape is derived from (read once, atomically).
  */
 #ifndef LAYERADAM_H
 #define LAYERADAM_H
@@ -74,7 +75,7 @@ typedef enum {
   LA_ERR_MISALIGNED = 2,       /* a buffer not 16-byte aligned              */
   LA_ERR_ALIASING = 3,         /* written ranges overlap each other or a
                                   gradient                                  */
-  LA_ERR_UNSUPPORTED = 4,      /* unknown gradient dtype                    */
+  LA_ERR_UNSUPPORTED = 4,      /* unknown gradient dtype or copy format     */
   LA_ERR_HIP = 5               /* the HIP runtime refused the launch        */
 } la_status;
 
