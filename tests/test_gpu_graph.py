@@ -97,3 +97,43 @@ def test_graph_with_a_device_step_counter_advances_t_every_replay():
         log(f"  replay t={t}: {rep}")
     assert int(t_dev.item()) == 7 and gl.flag.item() == 0
     gl.free()
+
+
+def test_device_step_matches_the_host_step_over_many_t():
+    """The constants that depend on t formed on the GPU (device pow in
+    double) against the host's: over about 270 step counts from 1 to 2^31 - 1,
+    m and v are bit-identical (they do not depend on t), the master is within
+    one FP32 ulp, and where the masters agree so do the compute copies."""
+    log("case device t vs host t")
+    n = 4096 + 13
+    w = synth.Workload(name="dstep_sweep", seed=5100, tensors=(("x", n),), replicas=2,
+                       grad_dtype="bf16", step=1)
+    L = synth.make_layer(w)
+    a, b = GpuLayer(L), GpuLayer(L)
+    la_a, la_b = la.Layer(a.params, a.grads), la.Layer(b.params, b.grads)
+    init = [x.clone() for x in a.params[0][:3]]
+    t_dev = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ts = sorted(set([1, 2, 3, 10, 100, 1000, 2**31 - 1]
+                    + np.unique(np.geomspace(1, 2**31 - 1, 293).astype(np.int64)).tolist()))
+    worst = 0
+    for t in ts:
+        for gl in (a, b):
+            for dst, src in zip(gl.params[0][:3], init):
+                dst.copy_(src)
+        t_dev.fill_(int(t))
+        la_a.step(step=int(t), **w.hyper)
+        la_b.step_device_step(t_dev, **w.hyper)
+        pa, pb = a.params[0], b.params[0]
+        assert torch.equal(pa[1], pb[1]) and torch.equal(pa[2], pb[2]), t
+        ia = pa[0].view(torch.int32).cpu().numpy().astype(np.int64)
+        ib = pb[0].view(torch.int32).cpu().numpy().astype(np.int64)
+        ia = np.where(ia < 0, -(ia & 0x7FFFFFFF), ia)
+        ib = np.where(ib < 0, -(ib & 0x7FFFFFFF), ib)
+        d = int(np.abs(ia - ib).max())
+        worst = max(worst, d)
+        assert d <= 1, (t, d)
+        if d == 0:
+            assert torch.equal(pa[3].view(torch.int16), pb[3].view(torch.int16)), t
+    log(f"  {len(ts)} step counts, worst master difference {worst} ulp")
+    a.free()
+    b.free()
