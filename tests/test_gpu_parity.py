@@ -126,6 +126,28 @@ def test_injected_non_finite_gradients(code):
         assert np.isnan(got["master"][i][j]) and got["weight_out"][i][j] == 0x7FC0
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_sums_past_the_gradient_format(dtype):
+    """The replicas are summed in FP32: eight FP16 gradients of +-65504 sum to
+    +-524032, far outside FP16 yet finite, so nothing is flagged; two BF16
+    gradients at the largest finite BF16 overflow FP32 itself, which is."""
+    w = synth.Workload(name=f"wide_sum_{dtype}", seed=2350, tensors=RAGGED, replicas=8,
+                       grad_dtype=dtype, step=5, with_flag=True)
+    ix = {name: i for i, (name, _) in enumerate(w.tensors)}
+
+    def mutate(L):
+        if dtype == "fp16":
+            for r in range(8):
+                L.grad(r, ix["k"])[:100] = 0x7BFF       # +65504
+                L.grad(r, ix["l"])[100:300] = 0xFBFF    # -65504
+        else:
+            for r in (3, 6):
+                L.grad(r, ix["n"])[77] = 0x7F7F         # largest finite BF16
+
+    got, _, _ = run_case(w, mutate)
+    assert got["flag"] == (1 if dtype == "bf16" else 0)
+
+
 def test_flag_stays_zero_and_is_never_cleared():
     w = synth.shrink(synth.WORKLOADS["flat_800m"], 4096)
     log("case flag sticky")
