@@ -202,6 +202,17 @@ LA_API la_status layer_adam_step_device_step(const la_layer_desc *layer,
                                              int32_t *overflow_flag,
                                              void *hip_stream);
 
+/* Measurement aid, not part of the update: enqueue a plain copy of `bytes`
+ * bytes from src to dst on `hip_stream`, with the update kernel's access
+ * style (16-byte non-temporal loads and stores, one workgroup per chunk) but
+ * one read and one write stream and no arithmetic -- the bandwidth a simple
+ * two-stream pattern reaches on this GPU, to read the update's rate against.
+ * bytes: a multiple of 16 (0 is a no-op); dst and src: device-addressable,
+ * 16-byte aligned, not overlapping. Status and errors as for
+ * layer_adam_step: checked on the host, nothing enqueued on failure. */
+LA_API la_status la_copy_reference(void *dst, const void *src, int64_t bytes,
+                                   void *hip_stream);
+
 /* Bytes of mixed-precision Adam state the layer stands for: 16 per
  * parameter (2 BF16 weight + 2 gradient + 4 FP32 master + 8 FP32 m and v).
  * -1 if the descriptor is invalid. Host only. */

@@ -30,8 +30,8 @@ OUT_BF16, OUT_FP16, OUT_NONE = 0, 1, 2
 
 # Exported symbols, as declared in include/layeradam.h.
 EXPORTS = ("layer_adam_step", "layer_adam_step_range", "layer_adam_step_gated",
-           "layer_adam_step_device_step", "la_check_gradients", "la_state_bytes", "la_traffic_bytes", "la_last_error",
-           "la_version")
+           "layer_adam_step_device_step", "la_check_gradients", "la_copy_reference",
+           "la_state_bytes", "la_traffic_bytes", "la_last_error", "la_version")
 
 
 class TensorDesc(ctypes.Structure):
@@ -165,6 +165,9 @@ def load(path: Optional[str] = None):
     lib.la_check_gradients.argtypes = [ctypes.POINTER(LayerDesc), ctypes.c_double,
                                        ctypes.c_void_p, ctypes.c_void_p]
     lib.la_check_gradients.restype = ctypes.c_int
+    lib.la_copy_reference.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                      ctypes.c_void_p]
+    lib.la_copy_reference.restype = ctypes.c_int
     lib.la_state_bytes.argtypes = [ctypes.POINTER(LayerDesc)]
     lib.la_state_bytes.restype = ctypes.c_int64
     lib.la_traffic_bytes.argtypes = [ctypes.POINTER(LayerDesc)]
@@ -484,6 +487,19 @@ class Layer:
 
     def traffic_bytes(self) -> int:
         return traffic_bytes_raw(self._desc)
+
+
+def copy_reference(dst, src, stream=None) -> None:
+    """la_copy_reference: copy the bytes of contiguous tensor src into dst
+    (same size, a multiple of 16 bytes) with the update's access style -- a
+    bandwidth reference, not part of the update."""
+    if src.nbytes != dst.nbytes:
+        raise ValueError(f"src has {src.nbytes} bytes, dst {dst.nbytes}")
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous")
+    lib = load()
+    _raise_on(lib.la_copy_reference(device_address(dst), device_address(src), src.nbytes,
+                                    _stream_ptr(stream) or None), lib)
 
 
 def state_bytes(numels: Sequence[int], num_replicas: int = 1) -> int:

@@ -16,6 +16,7 @@
 #include <cstring>
 #include <vector>
 
+#include "la_copy.h"
 #include "la_internal.h"
 #include "layeradam.h"
 
@@ -420,6 +421,32 @@ LA_API la_status la_check_gradients(const la_layer_desc* layer, double grad_unsc
   s.u = static_cast<float>(grad_unscale);
   return enqueue(layer, Mode::kCheck, s, la::DeviceStep{nullptr, 0.0, 0.0, 0.0}, 0,
                  total_numel(layer), found_nonfinite, nullptr, hip_stream);
+}
+
+LA_API la_status la_copy_reference(void* dst, const void* src, int64_t bytes,
+                                   void* hip_stream) {
+  if (bytes < 0 || bytes % 16 != 0)
+    return fail(LA_ERR_INVALID_ARGUMENT, "bytes = %lld, need a multiple of 16 >= 0",
+                static_cast<long long>(bytes));
+  if (bytes == 0) return ok();
+  if (dst == nullptr || src == nullptr)
+    return fail(LA_ERR_INVALID_ARGUMENT, "%s is NULL", dst == nullptr ? "dst" : "src");
+  if (!aligned(dst, LA_ALIGNMENT) || !aligned(src, LA_ALIGNMENT))
+    return fail(LA_ERR_MISALIGNED, "%s is not %d-byte aligned",
+                aligned(dst, LA_ALIGNMENT) ? "src" : "dst", LA_ALIGNMENT);
+  const uintptr_t d = reinterpret_cast<uintptr_t>(dst), s = reinterpret_cast<uintptr_t>(src);
+  const uintptr_t n = static_cast<uintptr_t>(bytes);
+  if (d < s + n && s < d + n) return fail(LA_ERR_ALIASING, "dst and src overlap");
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return fail(LA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  int lds_per_cu = 0, lds_per_block = 0;
+  device_facts(device, &lds_per_cu, &lds_per_block);
+  e = la::launch_copy_reference(dst, src, bytes / 16, lds_per_cu, lds_per_block,
+                                workgroups_per_cu_override(), static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess)
+    return fail(LA_ERR_HIP, "copy launch failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 LA_API int64_t la_state_bytes(const la_layer_desc* layer) {

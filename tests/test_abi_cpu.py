@@ -357,3 +357,18 @@ def test_binding_refuses_more_than_eight_replicas():
     grads = [[torch.zeros(8, dtype=torch.bfloat16)] * (la.MAX_REPLICAS + 1)]
     with pytest.raises(ValueError, match="at most 8"):
         la._describe([(p, p, p, None)], grads)
+
+
+@host_only
+def test_copy_reference_refusals():
+    """Every call here is invalid (or empty), so nothing is ever enqueued."""
+    lib = la.load()
+    a, b = 0x7F0000000000, 0x7F0100000000
+    cases = [(a, b, 24, 1), (a, b, -16, 1), (0, b, 1024, 1), (a, 0, 1024, 1),
+             (a + 8, b, 1024, 2), (a, b + 4, 1024, 2), (a, a + 512, 1024, 3),
+             (a + 1008, a, 1024, 3)]
+    for dst, src, n, want in cases:
+        rc = lib.la_copy_reference(ctypes.c_void_p(dst), ctypes.c_void_p(src), n, None)
+        assert rc == want, (hex(dst), hex(src), n, rc, la.last_error())
+        assert la.last_error()
+    assert lib.la_copy_reference(ctypes.c_void_p(a), ctypes.c_void_p(b), 0, None) == 0

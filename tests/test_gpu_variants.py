@@ -349,3 +349,21 @@ def test_binding_refuses_bad_device_scalars_without_launching():
         for x, y in zip(before[f], after[f]):
             assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), f
     gl.free()
+
+
+@pytest.mark.parametrize("units", [0, 1, 255, 256, 257, 1025, 3 * 4096 + 7, 25_000_003])
+def test_copy_reference_copies_exactly(units):
+    """The bandwidth-reference copy: every byte arrives, nothing past the end
+    is written (16-byte units; the kernel's chunk is 256 units)."""
+    log(f"case copy reference {units} x 16 B")
+    n = 16 * units
+    g = torch.Generator(device="cuda").manual_seed(units)
+    src = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda", generator=g)
+    big = torch.zeros(n + 4096, dtype=torch.uint8, device="cuda")
+    la.copy_reference(big[:n], src)
+    torch.cuda.synchronize()
+    assert torch.equal(big[:n], src)
+    assert int(big[n:].count_nonzero()) == 0
+    if n >= 32:
+        with pytest.raises(la.LayerAdamError, match="MISALIGNED"):
+            la.copy_reference(big[8:8 + n - 16], src[:n - 16])
