@@ -88,6 +88,10 @@ many[200]["exp_avg"] = many[17]["weight_out"] + 64 if many[17]["numel"] > 64 els
 d, k = la.make_layer(many, 2, 0)
 refused(lib.layer_adam_step(ctypes.byref(d), ctypes.byref(hp), None, None))
 assert lib.la_state_bytes(ctypes.byref(d)) > 0 and lib.la_traffic_bytes(ctypes.byref(d)) > 0
+# the reference copy: odd size, NULL, misaligned, overlapping
+for dst, src, n in ((BASE, BASE + 0x10000000, 24), (0, BASE, 1024), (BASE + 8, BASE + 0x10000000, 1024),
+                    (BASE, BASE + 512, 1024)):
+    refused(lib.la_copy_reference(ctypes.c_void_p(dst), ctypes.c_void_p(src), n, None))
 print("refusals", calls)
 '''
 
