@@ -61,6 +61,10 @@ MUTANTS = {
     "gradient check ignores the unscale": ("  float u = (float)unscale;\n  int found = 0;",
                                            "  float u = 1.0f;\n  int found = 0;"),
     "gradient check misses NaN": ("if (!isfinite(g)) found = 1;", "if (isinf(g)) found = 1;"),
+    "fp16 copy takes the bf16 cast": ("*weight_out = lao_round_fp16(p);",
+                                      "*weight_out = lao_round_bf16(p);"),
+    "copy cast before the step": ("if (out_dtype == LAO_OUT_BF16) *weight_out = lao_round_bf16(p);",
+                                  "if (out_dtype == LAO_OUT_BF16) *weight_out = lao_round_bf16(decayed);"),
     "L2 decay instead of decoupled": (
         "float g = lao_aggregate(x->grad, replicas, dtype, j, s.u);",
         "float g = lao_aggregate(x->grad, replicas, dtype, j, s.u) + (float)weight_decay * x->master[j];"),
