@@ -167,7 +167,11 @@ LA_API la_status layer_adam_step_range(const la_layer_desc *layer,
  * layer -- the left-to-right sum of its R replicas times grad_unscale, in
  * FP32, exactly as the update forms it -- is +-Inf or NaN. Never clears it.
  * Reads only the gradients, 2R bytes per parameter; it may stop reading
- * once it sees the flag already set. grad_unscale must be finite and > 0. */
+ * once it sees the flag already set. grad_unscale must be finite and > 0.
+ * The pages name FP16 gradients among the mixed-precision state ("SlideDP",
+ * 前置知识) but give no overflow rule; this pre-pass and the gated step below
+ * implement the usual loss-scaling reading: a step whose aggregated gradient
+ * holds a non-finite value is skipped as a whole, decided on the device. */
 LA_API la_status la_check_gradients(const la_layer_desc *layer,
                                     double grad_unscale,
                                     int32_t *found_nonfinite,
@@ -177,8 +181,9 @@ LA_API la_status la_check_gradients(const la_layer_desc *layer,
  * touched -- when the device int32 *skip_if_nonzero (4-byte aligned; may not
  * be NULL) holds a non-zero value when the kernel runs. With
  * la_check_gradients writing that flag for every layer first, a step whose
- * gradients overflowed is skipped without a host synchronisation (the usual
- * mixed-precision loss-scaling rule). The caller decides from the same flag,
+ * gradients overflowed is skipped without a host synchronisation (the
+ * loss-scaling reading of the FP16-gradient state of "SlideDP", 前置知识,
+ * described at la_check_gradients). The caller decides from the same flag,
  * once read, whether to count the step in t. */
 LA_API la_status layer_adam_step_gated(const la_layer_desc *layer,
                                        const la_adam_params *hp,
@@ -213,6 +218,21 @@ LA_API la_status layer_adam_step_device_step(const la_layer_desc *layer,
 LA_API la_status la_copy_reference(void *dst, const void *src, int64_t bytes,
                                    void *hip_stream);
 
+/* Measurement aid, not part of the update: the stream probe. Enqueue, on
+ * `hip_stream`, a pass over `layer` that moves exactly the bytes a
+ * layer_adam_step of the same layer moves, in exactly its launch shape (the
+ * same tensor table, chunks, workgroups and residency), with no arithmetic:
+ * it reads the R gradient replicas and master, m, v, writes master, m and v
+ * back unchanged, and writes the compute copy (unless LA_OUT_NONE) as the
+ * bitwise XOR of the replicas' 16-bit patterns -- so the copy is clobbered
+ * until the next update rewrites it. Its rate is what HBM gives this mix of
+ * R + 3 read and 4 write streams: the beta of the step-time bound
+ * T >= max_j W_j / beta_j ("SlideDP", 研究动机 and 技术新颖性) measured for
+ * the update's own access pattern. Arguments are checked as for
+ * layer_adam_step (no hyperparameters; the gradient dtype does not matter);
+ * nothing is enqueued on failure. */
+LA_API la_status la_stream_probe(const la_layer_desc *layer, void *hip_stream);
+
 /* Bytes of mixed-precision Adam state the layer stands for: 16 per
  * parameter (2 BF16 weight + 2 gradient + 4 FP32 master + 8 FP32 m and v).
  * -1 if the descriptor is invalid. Host only. */
@@ -220,8 +240,13 @@ LA_API int64_t la_state_bytes(const la_layer_desc *layer);
 
 /* Bytes one layer_adam_step moves to and from HBM in the ideal case:
  * (2R + 26) per parameter = R gradient reads + master, m, v read and written
- * + the 2-byte compute copy ((2R + 24) with LA_OUT_NONE). -1 if the
- * descriptor is invalid. Host only. */
+ * + the 2-byte compute copy ((2R + 24) with LA_OUT_NONE). This is the W of
+ * the one resource the update uses in the step-time bound T >= max_j W_j /
+ * beta_j of "SlideDP: Scaling Host-Resident LLM Fine-Tuning Across Multiple
+ * GPUs" (研究动机, and 技术新颖性 for the per-resource minimum duration
+ * W_j / beta_j): with HBM the only resource, a launch takes at least these
+ * bytes over the HBM bandwidth. -1 if the descriptor is invalid. Host
+ * only. */
 LA_API int64_t la_traffic_bytes(const la_layer_desc *layer);
 
 /* Message of the calling thread's last failed call ("" if none). The pointer

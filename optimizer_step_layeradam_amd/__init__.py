@@ -30,7 +30,8 @@ OUT_BF16, OUT_FP16, OUT_NONE = 0, 1, 2
 
 # Exported symbols, as declared in include/layeradam.h.
 EXPORTS = ("layer_adam_step", "layer_adam_step_range", "layer_adam_step_gated",
-           "layer_adam_step_device_step", "la_check_gradients", "la_copy_reference",
+           "layer_adam_step_device_step", "la_check_gradients", "la_stream_probe",
+           "la_copy_reference",
            "la_state_bytes", "la_traffic_bytes", "la_last_error", "la_version")
 
 
@@ -165,6 +166,8 @@ def load(path: Optional[str] = None):
     lib.la_check_gradients.argtypes = [ctypes.POINTER(LayerDesc), ctypes.c_double,
                                        ctypes.c_void_p, ctypes.c_void_p]
     lib.la_check_gradients.restype = ctypes.c_int
+    lib.la_stream_probe.argtypes = [ctypes.POINTER(LayerDesc), ctypes.c_void_p]
+    lib.la_stream_probe.restype = ctypes.c_int
     lib.la_copy_reference.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                       ctypes.c_void_p]
     lib.la_copy_reference.restype = ctypes.c_int
@@ -261,6 +264,12 @@ def check_gradients_raw(desc: LayerDesc, grad_unscale: float, found_nonfinite: i
     lib = load()
     _raise_on(lib.la_check_gradients(ctypes.byref(desc), float(grad_unscale),
                                      found_nonfinite or None, stream or None), lib)
+
+
+def stream_probe_raw(desc: LayerDesc, stream: int = 0) -> None:
+    """la_stream_probe on raw descriptors."""
+    lib = load()
+    _raise_on(lib.la_stream_probe(ctypes.byref(desc), stream or None), lib)
 
 
 def state_bytes_raw(desc: LayerDesc) -> int:
@@ -426,6 +435,16 @@ def step_device_step(params, grads, step_on_device, *, lr: float, beta1: float, 
     del keep
 
 
+def stream_probe(params, grads, *, stream=None) -> None:
+    """la_stream_probe: the update's loads, stores and launch shape without
+    its arithmetic (master, m, v rewritten unchanged; the compute copy
+    overwritten with the XOR of the replicas) -- a bandwidth measurement."""
+    tensors, R, gd, od = _describe(params, grads)
+    desc, keep = make_layer(tensors, R, gd, od)
+    stream_probe_raw(desc, _stream_ptr(stream))
+    del keep
+
+
 def check_gradients(grads, found_nonfinite, *, grad_unscale: float = 1.0, stream=None) -> None:
     """Set the int32 CUDA scalar ``found_nonfinite`` to 1 if some aggregated
     gradient (sum of the replicas times grad_unscale) is non-finite.
@@ -481,6 +500,9 @@ class Layer:
                         stream=None) -> None:
         check_gradients_raw(self._desc, grad_unscale,
                             _flag_ptr(found_nonfinite, "found_nonfinite"), _stream_ptr(stream))
+
+    def stream_probe(self, stream=None) -> None:
+        stream_probe_raw(self._desc, _stream_ptr(stream))
 
     def state_bytes(self) -> int:
         return state_bytes_raw(self._desc)

@@ -90,7 +90,9 @@ bool finite_nonneg(double x) { return std::isfinite(x) && x >= 0.0; }
 
 bool aligned(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
-enum class Mode { kUpdate, kCheck };
+// kUpdate: the update (state and copy written); kProbe: the stream probe
+// (the same buffers, no arithmetic); kCheck: gradients read only.
+enum class Mode { kUpdate, kProbe, kCheck };
 
 // Counts, dtypes and sizes; no pointers (enough for the byte accounting).
 la_status check_counts(const la_layer_desc* layer) {
@@ -125,7 +127,7 @@ la_status check_counts(const la_layer_desc* layer) {
 
 // Every buffer the mode touches: present and 16-byte aligned.
 la_status check_pointers(const la_layer_desc* layer, Mode mode) {
-  const bool state = mode == Mode::kUpdate;
+  const bool state = mode != Mode::kCheck;
   const bool out = state && layer->out_dtype != LA_OUT_NONE;
   for (int i = 0; i < layer->num_tensors; ++i) {
     const la_tensor_desc& t = layer->tensors[i];
@@ -166,7 +168,7 @@ la_status check_aliasing(const la_layer_desc* layer, Mode mode, const int32_t* f
                          const int32_t* skip, const int64_t* step = nullptr) {
   std::vector<Range> written;
   std::vector<Range> read;
-  const bool state = mode == Mode::kUpdate;
+  const bool state = mode != Mode::kCheck;
   const bool out = state && layer->out_dtype != LA_OUT_NONE;
   written.reserve(4 * layer->num_tensors + 1);
   read.reserve(layer->num_replicas * layer->num_tensors + 1);
@@ -276,7 +278,8 @@ la_status enqueue(const la_layer_desc* layer, Mode mode, const la::Scalars& s,
   hipStream_t stream = static_cast<hipStream_t>(hip_stream);
   la::LaunchShape shape{0, 0, 0, -1};
   const bool fp16 = layer->grad_dtype == LA_GRAD_FP16;
-  const bool out = mode == Mode::kUpdate && layer->out_dtype != LA_OUT_NONE;
+  const bool state = mode != Mode::kCheck;
+  const bool out = state && layer->out_dtype != LA_OUT_NONE;
 
   auto flush = [&]() -> la_status {
     if (pending == 0) return LA_OK;
@@ -289,12 +292,20 @@ la_status enqueue(const la_layer_desc* layer, Mode mode, const la::Scalars& s,
       device_facts(device, &shape.lds_per_cu, &shape.lds_per_block);
       shape.wg_per_cu = workgroups_per_cu_override();
     }
-    hipError_t e = mode == Mode::kUpdate
-                       ? la::launch_layer_adam(batch, pending, layer->num_replicas, fp16,
-                                               layer->out_dtype, s, dstep, flag, skip, stream,
-                                               shape)
-                       : la::launch_check_gradients(batch, pending, layer->num_replicas, fp16,
-                                                    s.u, flag, stream, shape);
+    hipError_t e;
+    switch (mode) {
+      case Mode::kUpdate:
+        e = la::launch_layer_adam(batch, pending, layer->num_replicas, fp16, layer->out_dtype, s,
+                                  dstep, flag, skip, stream, shape);
+        break;
+      case Mode::kProbe:
+        e = la::launch_stream_probe(batch, pending, layer->num_replicas, layer->out_dtype,
+                                    stream, shape);
+        break;
+      default:
+        e = la::launch_check_gradients(batch, pending, layer->num_replicas, fp16, s.u, flag,
+                                       stream, shape);
+    }
     if (e != hipSuccess)
       return fail(LA_ERR_HIP, "kernel launch %d failed: %s", launches, hipGetErrorString(e));
     ++launches;
@@ -303,7 +314,6 @@ la_status enqueue(const la_layer_desc* layer, Mode mode, const la::Scalars& s,
   };
   auto add = [&](const la_tensor_desc& t, int64_t first, int64_t count) -> la_status {
     la::TensorArgs& a = batch[pending++];
-    const bool state = mode == Mode::kUpdate;
     a.p = state ? t.master + first : nullptr;
     a.m = state ? t.exp_avg + first : nullptr;
     a.v = state ? t.exp_avg_sq + first : nullptr;
@@ -421,6 +431,15 @@ LA_API la_status la_check_gradients(const la_layer_desc* layer, double grad_unsc
   s.u = static_cast<float>(grad_unscale);
   return enqueue(layer, Mode::kCheck, s, la::DeviceStep{nullptr, 0.0, 0.0, 0.0}, 0,
                  total_numel(layer), found_nonfinite, nullptr, hip_stream);
+}
+
+LA_API la_status la_stream_probe(const la_layer_desc* layer, void* hip_stream) {
+  la_status st = check_counts(layer);
+  if (st != LA_OK) return st;
+  if ((st = check_pointers(layer, Mode::kProbe)) != LA_OK) return st;
+  if ((st = check_aliasing(layer, Mode::kProbe, nullptr, nullptr)) != LA_OK) return st;
+  return enqueue(layer, Mode::kProbe, la::Scalars{}, la::DeviceStep{nullptr, 0.0, 0.0, 0.0}, 0,
+                 total_numel(layer), nullptr, nullptr, hip_stream);
 }
 
 LA_API la_status la_copy_reference(void* dst, const void* src, int64_t bytes,

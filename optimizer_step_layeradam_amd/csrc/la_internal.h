@@ -68,6 +68,13 @@ hipError_t launch_layer_adam(const TensorArgs* tensors, int count, int replicas,
                              const DeviceStep& dstep, int32_t* flag, const int32_t* skip,
                              hipStream_t stream, const LaunchShape& shape);
 
+// Enqueue the stream probe over `count` tensors: the update's loads, stores
+// and launch shape with no arithmetic (master, m, v written back unchanged;
+// a 16-bit copy, unless out_dtype is kOutNone, written as the XOR of the
+// replicas' bit patterns).
+hipError_t launch_stream_probe(const TensorArgs* tensors, int count, int replicas,
+                               int out_dtype, hipStream_t stream, const LaunchShape& shape);
+
 // Enqueue the finite check of the aggregated gradients (sum of replicas times
 // unscale) of `count` tensors; sets *flag to 1 if one is +-Inf or NaN.
 hipError_t launch_check_gradients(const TensorArgs* tensors, int count, int replicas,

@@ -22,19 +22,20 @@
 // window of every stream, which measured faster on MI355X than a
 // persistent grid whose workgroups drift apart (the loop below still
 // strides by the grid when the grid is capped). A workgroup is one wave of
-// 64 lanes and a chunk two tiles of 64 x 4 elements: each lane owns 4
-// consecutive elements per tile and the two tiles are adjacent, so a wave
-// reads 2 KiB runs of each FP32 stream (16 B per lane) and 1 KiB runs of
-// each 16-bit gradient stream (8 B per lane), and a lane issues every load
-// of both tiles before any arithmetic, (12 + 2R) * 8 bytes in flight. The
+// 64 lanes and a chunk one tile of 64 x 4 elements: each lane owns 4
+// consecutive elements, so a wave reads a 1 KiB run of each FP32 stream
+// (16 B per lane) and a 512 B run of each 16-bit gradient stream (8 B per
+// lane), issues all R + 3 loads, computes, and issues its 4 stores. The
 // launch also reserves LDS that the kernel never touches, so that a compute
-// unit holds only a few of these waves at a time: 7 for R <= 4 replicas, 6
-// above. Fewer requests in flight interleave the R + 7 streams (R gradient
-// reads; master, m, v read and written; the compute copy) less at the HBM;
-// on the 14B-shaped layer this shape and these residencies measured fastest
-// at every R from 1 to 8 (against wider workgroups, more tiles per chunk and
-// other residencies). Every access carries the non-temporal hint: nothing
-// is reused.
+// unit holds only a few of these waves at a time -- 11 at R = 1 down to 8 at
+// R = 7, 8 (kResidency): about 40-55 KB of reads in flight per compute unit.
+// More requests in flight interleave the R + 7 streams (R gradient reads;
+// master, m, v read and written; the compute copy) worse at the HBM, fewer
+// leave it idle; the table is the measured best per R on the 14B-shaped
+// layer. Loads carry the non-temporal hint (nothing is reused); stores are
+// written through the L2 to memory (buffer stores with the sc0, sc1 and nt
+// policy bits), which measured 1-8 % faster than non-temporal write-back
+// stores, the most where writes are the largest share of the traffic.
 //
 // Arithmetic is IEEE binary32 with one rounding per operation: contraction
 // into fused multiply-adds is switched off for this file, and division and
@@ -50,9 +51,9 @@
 namespace la {
 namespace {
 
-// Tile shape, residency and cache hints. The defaults are the measured best
-// on MI355X for the Qwen3-14B-shaped layer at R = 1..8; the macros exist so
-// that other shapes can be built and compared.
+// Tile shape, residency and cache policy. The defaults are the measured best
+// on MI355X for the Qwen3-14B-shaped layer at R = 1..8 (and the other
+// layers); the macros exist so that other shapes can be built and compared.
 #ifndef LA_BLOCK
 #define LA_BLOCK 64
 #endif
@@ -60,27 +61,45 @@ namespace {
 #define LA_TILE_VEC 4
 #endif
 #ifndef LA_TILE_UNROLL
-#define LA_TILE_UNROLL 2
+#define LA_TILE_UNROLL 1
+#endif
+// With several tiles per chunk, the order of a chunk's loads (L), arithmetic
+// (C) and stores (S) per tile u, held by scheduling barriers: 0 = the
+// compiler's choice (no barriers); 1 = L0 L1 .. | C0 S0 | C1 S1 ..;
+// 2 = L0 L1 .. | C0 C1 .. | S0 S1 ..; 3 = L0 C0 S0 | L1 C1 S1 ..;
+// 4 = L0 C0 | L1 S0 C1 | L2 S1 C2 .. | S_last.
+#ifndef LA_SCHEDULE
+#define LA_SCHEDULE 0
 #endif
 #ifndef LA_NT_LOADS
 #define LA_NT_LOADS 1
 #endif
 #ifndef LA_NT_STORES
-#define LA_NT_STORES 1
+#define LA_NT_STORES 1   // global stores only (LA_BUFFER_STORES 0)
+#endif
+// Update and probe: 1 issues their loads (stores) as buffer instructions
+// with the cache-policy bits LA_LOAD_CPOL (LA_STORE_CPOL) -- 1 = sc0,
+// 2 = nt, 16 = sc1 -- instead of global instructions with the non-temporal
+// hint. Stores default to sc0 | sc1 | nt: written through to memory.
+#ifndef LA_BUFFER_LOADS
+#define LA_BUFFER_LOADS 0
+#endif
+#ifndef LA_BUFFER_STORES
+#define LA_BUFFER_STORES 1
+#endif
+#ifndef LA_LOAD_CPOL
+#define LA_LOAD_CPOL 2
+#endif
+#ifndef LA_STORE_CPOL
+#define LA_STORE_CPOL 19
 #endif
 #ifndef LA_WAVE_CONTIG
 #define LA_WAVE_CONTIG 1   // 1: each wave's tiles are adjacent in memory
 #endif
-// Update: resident workgroups per compute unit (0: no cap), for R up to
-// LA_FEW_REPLICAS and for more replicas.
-#ifndef LA_FEW_REPLICAS
-#define LA_FEW_REPLICAS 4
-#endif
-#ifndef LA_WORKGROUPS_PER_CU_FEW_REPLICAS
-#define LA_WORKGROUPS_PER_CU_FEW_REPLICAS 7
-#endif
+// Update: resident workgroups per compute unit for every R (0: no cap);
+// -1: the per-R table kResidency.
 #ifndef LA_WORKGROUPS_PER_CU
-#define LA_WORKGROUPS_PER_CU 6
+#define LA_WORKGROUPS_PER_CU -1
 #endif
 // The finite check only reads: more requests in flight help it (measured
 // 7.1 TB/s with 128-thread workgroups, 8 tiles per chunk and no residency
@@ -104,14 +123,19 @@ constexpr int kCheckBlock = LA_CHECK_BLOCK;
 constexpr int kCheckUnroll = LA_CHECK_TILE_UNROLL;
 constexpr int kCheckChunk = kCheckBlock * kVec * kCheckUnroll;
 static_assert(kVec == 4 || kVec == 8, "4 or 8 elements per thread per tile");
+static_assert(LA_SCHEDULE >= 0 && LA_SCHEDULE <= 4, "schedules 0 .. 4");
 static_assert(kBlock % 64 == 0 && kBlock <= 1024, "whole waves");
 static_assert(kCheckBlock % 64 == 0 && kCheckBlock <= 1024, "whole waves");
 static_assert(kChunk > kMaxUnalignedEntry && kCheckChunk > kMaxUnalignedEntry,
               "short unaligned entries must take the element-wise path");
 
+// Update residency per replica count (index R), the measured best of 6..12
+// per compute unit for one-tile chunks on the 14B-shaped layer.
+constexpr int kResidency[kMaxReplicas + 1] = {0, 11, 10, 10, 9, 9, 9, 8, 8};
+
 template <int R>
 constexpr int update_workgroups_per_cu() {
-  return R <= LA_FEW_REPLICAS ? LA_WORKGROUPS_PER_CU_FEW_REPLICAS : LA_WORKGROUPS_PER_CU;
+  return LA_WORKGROUPS_PER_CU >= 0 ? LA_WORKGROUPS_PER_CU : kResidency[R];
 }
 
 // Native vector types (the non-temporal builtins need them).
@@ -128,6 +152,41 @@ template <typename T>
 __device__ __forceinline__ void store_stream(T v, T* p) {
   if constexpr (LA_NT_STORES) __builtin_nontemporal_store(v, p);
   else *p = v;
+}
+
+// T (16 or 8 bytes) at element `elem` of a uniform base pointer.
+template <typename T, typename E>
+__device__ __forceinline__ T load_at(const E* base, uint32_t elem) {
+  if constexpr (LA_BUFFER_LOADS) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<E*>(base), 0, 0x7fffffff, 0x00020000);
+    const uint32_t byte = elem * static_cast<uint32_t>(sizeof(E));
+    if constexpr (sizeof(T) == 16)
+      return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, byte, 0, LA_LOAD_CPOL));
+    else
+      return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, byte, 0, LA_LOAD_CPOL));
+  } else {
+    return load_stream(reinterpret_cast<const T*>(base + elem));
+  }
+}
+
+template <typename T, typename E>
+__device__ __forceinline__ void store_at(T x, E* base, uint32_t elem) {
+  if constexpr (LA_BUFFER_STORES) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
+    const uint32_t byte = elem * static_cast<uint32_t>(sizeof(E));
+    if constexpr (sizeof(T) == 16)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, byte, 0,
+                                             LA_STORE_CPOL);
+    else
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), r, byte, 0,
+                                            LA_STORE_CPOL);
+  } else {
+    store_stream(x, reinterpret_cast<T*>(base + elem));
+  }
 }
 
 template <int R>
@@ -149,6 +208,7 @@ struct KernelArgs {
   const int32_t* skip;   // update only: skip everything if *skip != 0; or null
   DeviceStep dstep;      // update only: step count in device memory, or t == null
   int32_t count;
+  uint32_t key;          // probe only: XORed into the stored state; 0 from the host
 };
 
 // ---- gradient decode ------------------------------------------------------
@@ -251,25 +311,23 @@ __device__ __forceinline__ uint32_t tile_offset(int u, int tid) {
   }
 }
 
-// Store one tile's results: master, m, v as 16-byte vectors, the compute
-// copy packed two values per 32-bit word.
+// One tile's results in store order: master, m, v as 16-byte vectors, the
+// compute copy packed two values per 32-bit word.
+struct TileOut {
+  f32x4 P[kQuads], M[kQuads], V[kQuads];
+  half_words W;
+};
+
 template <int OUT>
-__device__ __forceinline__ void store_tile(const Elem* e, float* p, float* m, float* v,
+__device__ __forceinline__ void store_tile(const TileOut& y, float* p, float* m, float* v,
                                            uint16_t* w, uint32_t off) {
 #pragma unroll
   for (int q = 0; q < kQuads; ++q) {
-    const Elem* x = e + 4 * q;
-    store_stream(f32x4{x[0].p, x[1].p, x[2].p, x[3].p}, reinterpret_cast<f32x4*>(p + off) + q);
-    store_stream(f32x4{x[0].m, x[1].m, x[2].m, x[3].m}, reinterpret_cast<f32x4*>(m + off) + q);
-    store_stream(f32x4{x[0].v, x[1].v, x[2].v, x[3].v}, reinterpret_cast<f32x4*>(v + off) + q);
+    store_at(y.P[q], p, off + 4 * q);
+    store_at(y.M[q], m, off + 4 * q);
+    store_at(y.V[q], v, off + 4 * q);
   }
-  if constexpr (OUT != kOutNone) {
-    half_words wb;
-#pragma unroll
-    for (int k = 0; k < kVec; k += 2)
-      wb[k / 2] = out_bits<OUT>(e[k].p) | (out_bits<OUT>(e[k + 1].p) << 16);
-    store_stream(wb, reinterpret_cast<half_words*>(w + off));
-  }
+  if constexpr (OUT != kOutNone) store_at(y.W, w, off);
 }
 
 // Tensor of chunk c. Chunks only move forward within a workgroup, so t and
@@ -284,14 +342,92 @@ __device__ __forceinline__ void locate(const KernelArgs<R>& a, int64_t c, int& t
 }
 
 // ---- the update kernel ---------------------------------------------------------
+// What a launch computes. kHostStep: the update with the constants the host
+// derived. kDeviceStep: the same update with the step count read from device
+// memory when the kernel runs (alpha and q then formed on the GPU); only
+// these instantiations carry the double-precision pow. kProbe: no arithmetic
+// at all -- the stream probe, which moves exactly the update's bytes (R
+// gradient reads, master/m/v read and written back unchanged, the 16-bit copy
+// written as the XOR of the replicas' bit patterns) in exactly its launch
+// shape, to measure what HBM gives this stream mix.
+constexpr int kHostStep = 0;
+constexpr int kDeviceStep = 1;
+constexpr int kProbe = 2;
+
+// One tile of one lane: kVec elements of master, m, v and of every replica.
+template <int R>
+struct TileRegs {
+  f32x4 P[kQuads], M[kQuads], V[kQuads];
+  half_words G[R];
+};
+
+template <int R>
+__device__ __forceinline__ void load_tile(TileRegs<R>& x, const float* p, const float* m,
+                                          const float* v, const uint16_t* const (&g)[R],
+                                          uint32_t off) {
+#pragma unroll
+  for (int q = 0; q < kQuads; ++q) {
+    x.P[q] = load_at<f32x4>(p, off + 4 * q);
+    x.M[q] = load_at<f32x4>(m, off + 4 * q);
+    x.V[q] = load_at<f32x4>(v, off + 4 * q);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+    x.G[r] = load_at<half_words>(g[r], off);
+}
+
+// The update of one loaded tile.
 template <int R, bool FP16, bool FLAG, int OUT>
+__device__ __forceinline__ void update_tile(const TileRegs<R>& x, const Scalars& s, bool& bad,
+                                            TileOut& y) {
+  Elem e[kVec];
+#pragma unroll
+  for (int k = 0; k < kVec; ++k) {
+    const float gk = aggregate<R, FP16>(x.G, k, s.u);
+    if (FLAG) bad |= !__builtin_isfinite(gk);
+    e[k] = adam_update(gk, x.P[k / 4][k % 4], x.M[k / 4][k % 4], x.V[k / 4][k % 4], s);
+  }
+#pragma unroll
+  for (int q = 0; q < kQuads; ++q) {
+    const Elem* z = e + 4 * q;
+    y.P[q] = f32x4{z[0].p, z[1].p, z[2].p, z[3].p};
+    y.M[q] = f32x4{z[0].m, z[1].m, z[2].m, z[3].m};
+    y.V[q] = f32x4{z[0].v, z[1].v, z[2].v, z[3].v};
+  }
+  if constexpr (OUT != kOutNone) {
+#pragma unroll
+    for (int k = 0; k < kVec; k += 2)
+      y.W[k / 2] = out_bits<OUT>(e[k].p) | (out_bits<OUT>(e[k + 1].p) << 16);
+  }
+}
+
+// The probe's "arithmetic" for one loaded tile: master, m, v as loaded (XOR a
+// key the host passes as 0, so the compiler cannot drop a store of the value
+// it just loaded), the copy as the XOR of the replicas.
+template <int R, int OUT>
+__device__ __forceinline__ void probe_tile(const TileRegs<R>& x, uint32_t key, TileOut& y) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int q = 0; q < kQuads; ++q) {
+    y.P[q] = __builtin_bit_cast(f32x4, __builtin_bit_cast(u32x4, x.P[q]) ^ key);
+    y.M[q] = __builtin_bit_cast(f32x4, __builtin_bit_cast(u32x4, x.M[q]) ^ key);
+    y.V[q] = __builtin_bit_cast(f32x4, __builtin_bit_cast(u32x4, x.V[q]) ^ key);
+  }
+  if constexpr (OUT != kOutNone) {
+    y.W = x.G[0];
+#pragma unroll
+    for (int r = 1; r < R; ++r) y.W ^= x.G[r];
+  }
+}
+
+template <int R, bool FP16, bool FLAG, int OUT, int MODE>
 __global__ void __launch_bounds__(kBlock)
 layer_adam_kernel(const KernelArgs<R> a) {
   if (a.skip != nullptr && *a.skip != 0) return;  // gated step: overflowed, skip
   const int tid = threadIdx.x;
   const int64_t total_chunks = a.chunk_end[a.count - 1];
   Scalars s = a.s;
-  if (a.dstep.t != nullptr) {
+  if constexpr (MODE == kDeviceStep) {
     // Step count in device memory: the bias corrections of AdamW at the
     // 1-based step t, in double, each constant rounded once to FP32.
     const int64_t t = *a.dstep.t;
@@ -319,32 +455,68 @@ layer_adam_kernel(const KernelArgs<R> a) {
     for (int r = 0; r < R; ++r) g[r] = T.g[r] + base;
 
     if (base + kChunk <= n) {
-      // Full chunk: vector loads of every tile first, then the arithmetic.
-      f32x4 P[kUnroll][kQuads], M[kUnroll][kQuads], V[kUnroll][kQuads];
-      half_words G[kUnroll][R];
+      // Full chunk: loads, arithmetic and stores of every tile, in the
+      // order kSchedule names.
+      constexpr int kSchedule = LA_SCHEDULE;
+      TileRegs<R> x[kUnroll];
+      TileOut y[kUnroll];
+      auto load = [&](int u) {
+        load_tile<R>(x[u], p, m, v, g, tile_offset<kBlock, kUnroll>(u, tid));
+      };
+      auto compute = [&](int u) {
+        if constexpr (MODE == kProbe) probe_tile<R, OUT>(x[u], a.key, y[u]);
+        else update_tile<R, FP16, FLAG, OUT>(x[u], s, bad, y[u]);
+      };
+      auto store = [&](int u) {
+        store_tile<OUT>(y[u], p, m, v, w, tile_offset<kBlock, kUnroll>(u, tid));
+      };
+      auto fence = [] {
+        if constexpr (kSchedule != 0) __builtin_amdgcn_sched_barrier(0);
+      };
+      if constexpr (kSchedule <= 2) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const uint32_t off = tile_offset<kBlock, kUnroll>(u, tid);
-#pragma unroll
-        for (int q = 0; q < kQuads; ++q) {
-          P[u][q] = load_stream(reinterpret_cast<const f32x4*>(p + off) + q);
-          M[u][q] = load_stream(reinterpret_cast<const f32x4*>(m + off) + q);
-          V[u][q] = load_stream(reinterpret_cast<const f32x4*>(v + off) + q);
-        }
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-          G[u][r] = load_stream(reinterpret_cast<const half_words*>(g[r] + off));
+        for (int u = 0; u < kUnroll; ++u) load(u);
+        fence();
       }
+      if constexpr (kSchedule <= 1) {
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        Elem e[kVec];
-#pragma unroll
-        for (int k = 0; k < kVec; ++k) {
-          const float gk = aggregate<R, FP16>(G[u], k, s.u);
-          if (FLAG) bad |= !__builtin_isfinite(gk);
-          e[k] = adam_update(gk, P[u][k / 4][k % 4], M[u][k / 4][k % 4], V[u][k / 4][k % 4], s);
+        for (int u = 0; u < kUnroll; ++u) {
+          compute(u);
+          fence();
+          store(u);
+          fence();
         }
-        store_tile<OUT>(e, p, m, v, w, tile_offset<kBlock, kUnroll>(u, tid));
+      } else if constexpr (kSchedule == 2) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) compute(u);
+        fence();
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) store(u);
+      } else if constexpr (kSchedule == 3) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          load(u);
+          fence();
+          compute(u);
+          fence();
+          store(u);
+          fence();
+        }
+      } else {
+        load(0);
+        fence();
+        compute(0);
+        fence();
+#pragma unroll
+        for (int u = 1; u < kUnroll; ++u) {
+          load(u);
+          fence();
+          store(u - 1);
+          fence();
+          compute(u);
+          fence();
+        }
+        store(kUnroll - 1);
       }
     } else {
       // Last, partial chunk of a tensor: element by element, bounds-checked.
@@ -355,13 +527,25 @@ layer_adam_kernel(const KernelArgs<R> a) {
         for (int k = 0; k < kVec; ++k) {
           const int64_t i = static_cast<int64_t>((u * kBlock + tid) * kVec + k);
           if (i < left) {
-            const float gk = aggregate_one<R, FP16>(g, i, s.u);
-            if (FLAG) bad |= !__builtin_isfinite(gk);
-            const Elem e = adam_update(gk, p[i], m[i], v[i], s);
-            p[i] = e.p;
-            m[i] = e.m;
-            v[i] = e.v;
-            if constexpr (OUT != kOutNone) w[i] = static_cast<uint16_t>(out_bits<OUT>(e.p));
+            if constexpr (MODE == kProbe) {
+              p[i] = __uint_as_float(__float_as_uint(p[i]) ^ a.key);
+              m[i] = __uint_as_float(__float_as_uint(m[i]) ^ a.key);
+              v[i] = __uint_as_float(__float_as_uint(v[i]) ^ a.key);
+              if constexpr (OUT != kOutNone) {
+                uint16_t x = g[0][i];
+#pragma unroll
+                for (int r = 1; r < R; ++r) x ^= g[r][i];
+                w[i] = x;
+              }
+            } else {
+              const float gk = aggregate_one<R, FP16>(g, i, s.u);
+              if (FLAG) bad |= !__builtin_isfinite(gk);
+              const Elem e = adam_update(gk, p[i], m[i], v[i], s);
+              p[i] = e.p;
+              m[i] = e.m;
+              v[i] = e.v;
+              if constexpr (OUT != kOutNone) w[i] = static_cast<uint16_t>(out_bits<OUT>(e.p));
+            }
           }
         }
       }
@@ -462,7 +646,7 @@ hipError_t launch(const void* kernel, void* args, int64_t chunks, int block, int
                          static_cast<unsigned>(lds), stream);
 }
 
-template <int R, bool FP16, bool FLAG, int OUT>
+template <int R, bool FP16, bool FLAG, int OUT, int MODE>
 hipError_t launch_update_typed(const TensorArgs* ts, int count, const Scalars& s,
                                const DeviceStep& dstep, int32_t* flag, const int32_t* skip,
                                hipStream_t stream, const LaunchShape& shape) {
@@ -472,7 +656,8 @@ hipError_t launch_update_typed(const TensorArgs* ts, int count, const Scalars& s
   a.dstep = dstep;
   a.flag = flag;
   a.skip = skip;
-  return launch(reinterpret_cast<const void*>(&layer_adam_kernel<R, FP16, FLAG, OUT>), &a,
+  a.key = 0;
+  return launch(reinterpret_cast<const void*>(&layer_adam_kernel<R, FP16, FLAG, OUT, MODE>), &a,
                 chunks, kBlock, lds_reservation(shape, update_workgroups_per_cu<R>()), stream,
                 shape);
 }
@@ -481,8 +666,15 @@ template <int R, bool FP16, int OUT>
 hipError_t launch_update_flag(const TensorArgs* ts, int count, const Scalars& s,
                               const DeviceStep& d, int32_t* flag, const int32_t* skip,
                               hipStream_t stream, const LaunchShape& shape) {
-  return flag ? launch_update_typed<R, FP16, true, OUT>(ts, count, s, d, flag, skip, stream, shape)
-              : launch_update_typed<R, FP16, false, OUT>(ts, count, s, d, flag, skip, stream, shape);
+  if (d.t != nullptr)
+    return flag ? launch_update_typed<R, FP16, true, OUT, kDeviceStep>(ts, count, s, d, flag,
+                                                                       skip, stream, shape)
+                : launch_update_typed<R, FP16, false, OUT, kDeviceStep>(ts, count, s, d, flag,
+                                                                        skip, stream, shape);
+  return flag ? launch_update_typed<R, FP16, true, OUT, kHostStep>(ts, count, s, d, flag, skip,
+                                                                   stream, shape)
+              : launch_update_typed<R, FP16, false, OUT, kHostStep>(ts, count, s, d, flag, skip,
+                                                                    stream, shape);
 }
 
 template <int R, bool FP16>
@@ -503,6 +695,22 @@ hipError_t launch_update_r(const TensorArgs* ts, int count, bool fp16, int out,
                            const int32_t* skip, hipStream_t stream, const LaunchShape& shape) {
   return fp16 ? launch_update_out<R, true>(ts, count, out, s, d, flag, skip, stream, shape)
               : launch_update_out<R, false>(ts, count, out, s, d, flag, skip, stream, shape);
+}
+
+// The probe moves bit patterns only: the gradient format does not matter, and
+// both 16-bit copy formats are one 2-byte store.
+template <int R>
+hipError_t launch_probe_r(const TensorArgs* ts, int count, int out, hipStream_t stream,
+                          const LaunchShape& shape) {
+  const Scalars none = {};
+  const DeviceStep host = {nullptr, 0.0, 0.0, 0.0};
+  return out == kOutNone
+             ? launch_update_typed<R, false, false, kOutNone, kProbe>(ts, count, none, host,
+                                                                      nullptr, nullptr, stream,
+                                                                      shape)
+             : launch_update_typed<R, false, false, kOutBf16, kProbe>(ts, count, none, host,
+                                                                      nullptr, nullptr, stream,
+                                                                      shape);
 }
 
 template <int R>
@@ -529,6 +737,17 @@ hipError_t launch_layer_adam(const TensorArgs* tensors, int count, int replicas,
   case RR:                                                                                 \
     return launch_update_r<RR>(tensors, count, fp16, out_dtype, s, dstep, flag, skip,    \
                                stream, shape);
+    LA_CASE(1) LA_CASE(2) LA_CASE(3) LA_CASE(4) LA_CASE(5) LA_CASE(6) LA_CASE(7) LA_CASE(8)
+#undef LA_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_stream_probe(const TensorArgs* tensors, int count, int replicas,
+                               int out_dtype, hipStream_t stream, const LaunchShape& shape) {
+  switch (replicas) {
+#define LA_CASE(RR) \
+  case RR: return launch_probe_r<RR>(tensors, count, out_dtype, stream, shape);
     LA_CASE(1) LA_CASE(2) LA_CASE(3) LA_CASE(4) LA_CASE(5) LA_CASE(6) LA_CASE(7) LA_CASE(8)
 #undef LA_CASE
     default: return hipErrorInvalidValue;
