@@ -15,6 +15,12 @@ Prints one JSON line:
                the launch stream, against 8 TB/s; traffic = HBM bytes per
                launch from the committed rocprofv3 counter summary (null if
                the kernel source changed since it was taken)
+  stream_probe the library's stream probe on the same layer: the update's
+               loads, stores and launch shape without its arithmetic -- the
+               rate HBM gives this mix of R + 3 read and 4 write streams
+  per_workload every workload in turn (inputs drawn, uploaded, timed, freed):
+               mean launch time of the update and of the probe, Gparam/s,
+               GB/s and fraction of 8 TB/s
   cpu_baseline the CPU oracle timed on this host (one core) on a bounded
                prefix of the same layer, with its parity against the GPU's
                first step on that prefix
@@ -36,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "LayerAdam Gparam/s + HBM GB/s (% of peak), Qwen3-14B-shaped layer, R=8"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+WARM_MS = 50.0  # untimed traffic before each per-workload measurement
 KERNEL_SOURCES = ("optimizer_step_layeradam_amd/csrc/la_kernel.hip",
                   "optimizer_step_layeradam_amd/csrc/la_internal.h")
 COUNTERS = os.path.join(ROOT, "profiles", "layeradam_counters.json")
@@ -269,11 +276,19 @@ def host_link_reference(torch, mib: int = 1024, reps: int = 5):
     return out
 
 
-def time_launches(torch, fn, reps=10, warm=2):
-    """Mean milliseconds of fn() over reps, HIP events on the current stream."""
+def time_launches(torch, fn, reps=10, warm=2, warm_ms=0.0):
+    """Mean milliseconds of fn() over reps, HIP events on the current stream,
+    after `warm` untimed calls and then more until warm_ms of wall time has
+    passed (a freshly uploaded layer runs a few percent slower for its first
+    tens of milliseconds of traffic)."""
     for _ in range(warm):
         fn()
     torch.cuda.synchronize()
+    t_end = time.perf_counter() + warm_ms / 1e3
+    while time.perf_counter() < t_end:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
@@ -283,6 +298,151 @@ def time_launches(torch, fn, reps=10, warm=2):
         b.record(stream)
     torch.cuda.synchronize()
     return statistics.fmean(a.elapsed_time(b) for a, b in ev)
+
+
+def rates(w, ms):
+    """Gparam/s, GB/s under the (2R + 26)-byte model and fraction of 8 TB/s for
+    one launch of ms milliseconds over workload w."""
+    gbs = w.traffic_bytes / ms / 1e6
+    return {"ms": ms, "gparams": w.numel / ms / 1e6, "gbs": gbs, "frac": gbs / PEAK_HBM_GBS}
+
+
+def stream_probe(torch, layer, w, reps=20):
+    """The stream probe on the resident layer (mean launch time, HIP events)."""
+    return dict(rates(w, time_launches(torch, layer.stream_probe, reps=reps, warm=3,
+                                       warm_ms=WARM_MS)),
+                kernel="layer_adam_kernel (probe mode: no arithmetic)")
+
+
+def per_workload(torch, la, synth, reps=20):
+    """Every workload in turn: draw, upload, time the update and the probe
+    (mean launch time over reps launches, HIP events), free."""
+    import numpy as np
+    out = {}
+    for name, w in synth.WORKLOADS.items():
+        t_draw = time.time()
+        L = synth.make_layer(w)
+        params, grads, flat = upload(L, torch)
+        del L
+        log(f"bench: per-workload {name}: inputs resident after {time.time() - t_draw:.1f}s")
+        flag = torch.zeros(1, dtype=torch.int32, device="cuda:0") if w.with_flag else None
+        layer = la.Layer(params, grads)
+        t = [w.step]
+
+        def one():
+            layer.step(step=t[0], grad_unscale=w.unscale, overflow_flag=flag, **w.hyper)
+            t[0] += 1
+
+        entry = {"params": w.numel, "replicas": w.replicas, "grad_dtype": w.grad_dtype,
+                 "bytes_per_param": w.bytes_per_param,
+                 "update": rates(w, time_launches(torch, one, reps=reps, warm=3,
+                                                  warm_ms=WARM_MS)),
+                 "probe": stream_probe(torch, layer, w, reps=reps)}
+        entry["update_over_probe"] = entry["update"]["gbs"] / entry["probe"]["gbs"]
+        if flag is not None:
+            entry["overflow_flag"] = int(flag.item())
+        if w.traffic_bytes < 256 << 20:
+            entry["note"] = ("cache-resident (the whole layer fits in the caches) and "
+                             "launch-bound: not an HBM measurement")
+        out[name] = entry
+        del layer, params, grads, flat, flag
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
+
+
+def producer_overlap(torch, la, w, L, params, grads, flat, t0, k=1024, reps=3,
+                     host_link=True):
+    """Per-chunk release behind a gradient producer, with 64 MiB chunks per
+    replica. Producers (synth.producer): a GEMM on the GPU (the gradients
+    times the k x k identity, 2k flops per element, values unchanged) and DMA
+    from pinned host memory over the host link. After each chunk the producer
+    stream records an event; on a side stream the update of that chunk waits
+    on it and runs while the producer continues. Reports, per producer, the
+    producer alone, the chunked update alone and the two overlapped (wall
+    time between HIP events), and whether the gradients came out unchanged."""
+    from synth.producer import GemmProducer, HostLinkProducer, flat_to_layer
+    chunk = (64 << 20) // 2
+    sizes = [n for _, n in w.tensors]
+    layer = la.Layer(params, grads)
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    t = [t0]
+
+    def hp():
+        t[0] += 1
+        return dict(step=t[0], grad_unscale=w.unscale, **w.hyper)
+
+    def timed(body):
+        ms = []
+        for rep in range(reps + 1):
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(main)
+            end_stream = body(a)
+            b.record(end_stream)
+            torch.cuda.synchronize()
+            if rep:
+                ms.append(a.elapsed_time(b))
+        return statistics.fmean(ms)
+
+    def measure(prod, src):
+        ranges = [tuple(flat_to_layer(L.grad_offsets, sizes, x) for x in ab)
+                  for ab in prod.bounds]
+
+        def producer_alone(_):
+            for c in range(len(prod.bounds)):
+                prod.produce(c)
+            return main
+
+        def update_alone(_):
+            for lo, hi in ranges:
+                layer.step_range(lo, hi, **hp())
+            return main
+
+        def overlapped(start):
+            side.wait_event(start)
+            for c, (lo, hi) in enumerate(ranges):
+                prod.produce(c)
+                ready = torch.cuda.Event()
+                ready.record(main)
+                side.wait_event(ready)
+                layer.step_range(lo, hi, stream=side, **hp())
+            return side
+
+        p_ms, u_ms, o_ms = timed(producer_alone), timed(update_alone), timed(overlapped)
+        main.wait_stream(side)
+        torch.cuda.synchronize()
+        # the producer wrote the original values back (+0 and -0 alike)
+        same = all(bool(((s.to(d.device).view(torch.int16) == d.view(torch.int16)) |
+                         ((s.to(d.device) == 0) & (d == 0))).all())
+                   for s, d in zip(src, flat))
+        return {"chunks": len(prod.bounds), "producer_ms": p_ms, "update_ms": u_ms,
+                "overlapped_ms": o_ms, "serial_ms": p_ms + u_ms,
+                "overlapped_over_max": o_ms / max(p_ms, u_ms),
+                "update_hidden_fraction": (p_ms + u_ms - o_ms) / u_ms,
+                "gradients_reproduced": same}
+
+    out = {"chunk_bytes_per_replica": chunk * 2}
+    src = [g.clone() for g in flat]
+    prod = GemmProducer(src, flat, chunk_elems=chunk, k=k)
+    out["gemm"] = measure(prod, src)
+    out["gemm"]["gemm_k"] = k
+    out["gemm"]["producer_tflops"] = (prod.flops_per_chunk * len(prod.bounds) /
+                                      out["gemm"]["producer_ms"] / 1e9)
+    del src, prod
+    torch.cuda.empty_cache()
+    if not host_link:
+        return out
+    host = [torch.empty(g.shape, dtype=g.dtype, pin_memory=True) for g in flat]
+    for h, g in zip(host, flat):
+        h.copy_(g)
+    prod = HostLinkProducer(host, flat, chunk_elems=chunk)
+    out["host_link"] = measure(prod, host)
+    out["host_link"]["producer_gbs"] = (prod.bytes_per_chunk * len(prod.bounds) /
+                                        out["host_link"]["producer_ms"] / 1e6)
+    del host, prod
+    return out
 
 
 def extras(torch, la, w, params, grads, t0):
@@ -402,6 +562,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the neighbouring entry points timed after the main region")
+    ap.add_argument("--no-per-workload", action="store_true",
+                    help="skip timing every workload after the main region")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -511,12 +673,27 @@ def main():
                      "median_launch_ms": statistics.median(launch_ms),
                      "min_launch_ms": min(launch_ms), "max_launch_ms": max(launch_ms)},
         "overflow_flag_first_step": flag_first,
+        "stream_probe": stream_probe(torch, layer, w),
         "hbm_copy_reference": copy_reference(torch, la),
-        "extras": None if args.no_extras else extras(torch, la, w, params, grads, t),
+        "extras": None,
+        "per_workload": None,
         "cpu_baseline": None,
     }
-    # the update's rate against the plain two-stream copy measured above
+    # the update's rate against the probe of its own stream mix and launch
+    # shape, and against a plain two-stream copy
+    out["roofline"]["stream_probe_gbs"] = out["stream_probe"]["gbs"]
+    out["roofline"]["frac_of_stream_probe"] = achieved / out["stream_probe"]["gbs"]
     out["roofline"]["frac_of_copy_reference"] = achieved / out["hbm_copy_reference"]["gbs"]
+    if not args.no_extras:
+        out["extras"] = extras(torch, la, w, params, grads, t)
+        log("bench: producer overlap")
+        out["extras"]["producer_overlap"] = producer_overlap(torch, la, w, L, params, grads,
+                                                             _flat, t + 1000)
+    del layer, params, grads, _flat
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_per_workload:
+        out["per_workload"] = per_workload(torch, la, synth)
     if first is not None:
         log("bench: CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(L, first, args.cpu_seconds)

@@ -8,6 +8,8 @@ the oracle's RNE cast of the GPU's own master and against the oracle's BF16.
 from __future__ import annotations
 
 import sys
+import threading
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 from typing import Dict, List, Optional, Sequence
 
@@ -189,13 +191,52 @@ def compare(gpu: Dict[str, List[np.ndarray]], ts, idx=None, report: Optional[Rep
     return rep
 
 
-def sample_indices(w: synth.Workload, per_tensor: int, seed: int = 0) -> List[np.ndarray]:
-    """Sorted unique indices per tensor: the first and last 4096 elements, the
-    whole final chunk region, and `per_tensor` uniform draws."""
-    rng = np.random.default_rng(seed)
+def slices_of(w: synth.Workload, size: int):
+    """(tensor, begin, end) for every tensor cut into slices of ``size``."""
     out = []
-    for _, n in w.tensors:
-        parts = [np.arange(min(n, 4096)), np.arange(max(0, n - 8192), n),
-                 rng.integers(0, n, min(n, per_tensor))]
-        out.append(np.unique(np.concatenate(parts)).astype(np.int64))
+    for i, (_, n) in enumerate(w.tensors):
+        for a in range(0, n, size):
+            out.append((i, a, min(n, a + size)))
     return out
+
+
+def compare_every_element(gl: GpuLayer, L: synth.LayerInputs, slice_size: int = 1 << 24,
+                          threads: int = 16, label: str = "", **hp_over):
+    """Compare every element of the GPU's state and compute copy after one
+    step (already taken on ``gl``) with the oracle run on the same inputs,
+    one slice at a time: each worker downloads a slice of master/m/v/copy,
+    runs the oracle on the matching input slice and compares, so host memory
+    stays bounded by threads x slice. Returns (Report, oracle flag)."""
+    w = L.workload
+    torch.cuda.synchronize()
+    lock = threading.Lock()
+    total = Report()
+    flags = []
+
+    def one(item):
+        i, a, b = item
+        p, m, v, _ = gl.params[i]
+        wb = gl.out_buffers[i]
+        got = {"master": [p[a:b].cpu().numpy()], "exp_avg": [m[a:b].cpu().numpy()],
+               "exp_avg_sq": [v[a:b].cpu().numpy()],
+               "weight_out": [wb.view(torch.int16)[a:b].cpu().numpy().view(np.uint16)]}
+        ts = [oracle.Tensor(np.array(L.master[i][a:b], np.float32),
+                            np.array(L.exp_avg[i][a:b], np.float32),
+                            np.array(L.exp_avg_sq[i][a:b], np.float32),
+                            np.zeros(b - a, np.uint16),
+                            [np.ascontiguousarray(L.grad(r, i)[a:b])
+                             for r in range(w.replicas)])]
+        flag = oracle_step(L, ts, **hp_over)
+        rep = compare(got, ts, label=f"{label} tensor {i} [{a}, {b})", out=gl.out)
+        with lock:
+            total.compared += rep.compared
+            total.max_ulp = max(total.max_ulp, rep.max_ulp)
+            total.nonzero_ulp += rep.nonzero_ulp
+            total.bf16_mismatch += rep.bf16_mismatch
+            flags.append(flag or 0)
+
+    with ThreadPoolExecutor(threads) as ex:
+        for _ in ex.map(one, slices_of(w, slice_size)):
+            pass
+    assert total.compared == w.numel, (total.compared, w.numel)
+    return total, max(flags) if flags else 0

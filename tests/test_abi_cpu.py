@@ -372,3 +372,38 @@ def test_copy_reference_refusals():
         assert rc == want, (hex(dst), hex(src), n, rc, la.last_error())
         assert la.last_error()
     assert lib.la_copy_reference(ctypes.c_void_p(a), ctypes.c_void_p(b), 0, None) == 0
+
+
+@host_only
+@pytest.mark.parametrize("case", ["null_master", "null_grad", "misaligned_v", "m_on_master",
+                                  "grad_on_copy", "bad_out", "R9"])
+def test_stream_probe_refusals(case):
+    """The stream probe checks its buffers as the update does (it writes
+    master, m, v and the copy); nothing reaches the device on a refusal."""
+    t, R, out = fake_tensor(0), 2, la.OUT_BF16
+    if case == "null_master":
+        t["master"] = 0
+    elif case == "null_grad":
+        t["grads"][1] = 0
+    elif case == "misaligned_v":
+        t["exp_avg_sq"] += 4
+    elif case == "m_on_master":
+        t["exp_avg"] = t["master"] + 256
+    elif case == "grad_on_copy":
+        t["grads"][0] = t["weight_out"] + 32
+    elif case == "bad_out":
+        out = 7
+    elif case == "R9":
+        R = 9
+    desc, keep = la.make_layer([t], R, la.GRAD_BF16, out)
+    with pytest.raises(la.LayerAdamError) as e:
+        la.stream_probe_raw(desc)
+    assert e.value.status == {"null_master": 1, "null_grad": 1, "misaligned_v": 2,
+                              "m_on_master": 3, "grad_on_copy": 3, "bad_out": 4,
+                              "R9": 1}[case]
+
+
+def test_stream_probe_of_an_empty_layer_enqueues_nothing():
+    desc, keep = la.make_layer([dict(numel=0)], 2, la.GRAD_BF16)
+    la.stream_probe_raw(desc)
+    assert la.last_error() == ""

@@ -12,8 +12,8 @@ import torch
 import optimizer_step_layeradam_amd as la
 import oracle
 import synth
-from lahelpers import (RAGGED, GpuLayer, Report, compare, log, oracle_step, oracle_tensors,
-                       sample_indices)
+from lahelpers import (RAGGED, GpuLayer, Report, compare, compare_every_element, log,
+                       oracle_step, oracle_tensors)
 
 pytestmark = pytest.mark.gpu
 
@@ -287,11 +287,9 @@ def test_bad_buffers_are_refused_before_any_work():
 
 
 # ---------------------------------------------------------------------------
-# Full sizes, in the benchmark's launch configuration
+# Full sizes, in the benchmark's launch configuration: every element of every
+# workload against the oracle, slice by slice on 16 host threads
 # ---------------------------------------------------------------------------
-FULL_COMPARE = ("tiny", "qwen3_4b_layer", "qwen3_14b_layer")
-
-
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
 def test_workload_full_size(name):
     w = synth.WORKLOADS[name]
@@ -302,34 +300,10 @@ def test_workload_full_size(name):
     log("  GPU step")
     gl.step()
     torch.cuda.synchronize()
-    if name in FULL_COMPARE:
-        got = gl.download()
-        gl.free()
-        log("  oracle on every element")
-        ts = oracle_tensors(L)
-        flag = oracle_step(L, ts)
-        rep = compare(got, ts, label=name)
-    else:
-        # every element: the BF16 copy is the RNE cast of the new master
-        # (torch's float32 -> bfloat16 is round-to-nearest-even; no NaN here)
-        for p, _, _, wb in gl.params:
-            assert torch.equal(p.to(torch.bfloat16).view(torch.int16), wb.view(torch.int16))
-            assert bool(torch.isfinite(p).all())
-        idx = sample_indices(w, per_tensor=400_000, seed=5)
-        log(f"  oracle on {sum(i.size for i in idx)} sampled elements")
-        torch.cuda.synchronize()
-        got = {"master": [], "exp_avg": [], "exp_avg_sq": [], "weight_out": []}
-        for (p, m, v, wb), ii in zip(gl.params, idx):
-            it = torch.from_numpy(ii).to(p.device)
-            got["master"].append(p[it].cpu().numpy())
-            got["exp_avg"].append(m[it].cpu().numpy())
-            got["exp_avg_sq"].append(v[it].cpu().numpy())
-            got["weight_out"].append(wb.view(torch.int16)[it].cpu().numpy().view(np.uint16))
-        got["flag"] = int(gl.flag.item())
-        gl.free()
-        ts = oracle_tensors(L, idx)
-        flag = oracle_step(L, ts)
-        rep = compare(got, ts, label=name)
+    log("  oracle on every element, slice by slice")
+    rep, flag = compare_every_element(gl, L, label=name)
+    got_flag = int(gl.flag.item())
+    gl.free()
     if w.with_flag:
-        assert got["flag"] == flag == 0
+        assert got_flag == flag == 0
     log(f"  {rep}")

@@ -120,6 +120,52 @@ def test_fixed_size_chunks_over_a_layer():
     gl.free()
 
 
+@pytest.mark.parametrize("name", ["qwen3_14b_layer", "flat_800m"])
+def test_update_overlaps_a_gradient_producer(name):
+    """Per-chunk release with a real producer: on one stream a GEMM writes each
+    chunk of every gradient replica (the seeded gradients times the identity,
+    so the values are exactly the seeded ones); after each chunk it records an
+    event, and on a second stream the update of that chunk waits on the event
+    and runs while the producer moves on. Every element is compared with the
+    oracle afterwards."""
+    w = synth.shrink(synth.WORKLOADS[name], 16)
+    log(f"case producer overlap {w.name}: N={w.numel} R={w.replicas}")
+    L = synth.make_layer(w)
+    gl = GpuLayer(L)
+    from synth.producer import GemmProducer, flat_to_layer
+    src = [g.clone() for g in gl.grad_flat]
+    for g in gl.grad_flat:
+        g.zero_()
+    k = 256
+    prod = GemmProducer(src, gl.grad_flat, chunk_elems=2048 * k, k=k)
+    sizes = [n for _, n in w.tensors]
+    layer = la.Layer(gl.params, gl.grads)
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    side.wait_stream(main)
+    for c, (a, b) in enumerate(prod.bounds):
+        prod.produce(c)
+        ready = torch.cuda.Event()
+        ready.record(main)
+        side.wait_event(ready)
+        lo, hi = (flat_to_layer(L.grad_offsets, sizes, x) for x in (a, b))
+        layer.step_range(lo, hi, step=w.step, grad_unscale=w.unscale,
+                         overflow_flag=gl.flag if w.with_flag else None, stream=side, **w.hyper)
+    main.wait_stream(side)
+    torch.cuda.synchronize()
+    assert len(prod.bounds) > 10
+    for s, d in zip(src, gl.grad_flat):  # the producer wrote the seeded values (+-0 aside)
+        same = (s.view(torch.int16) == d.view(torch.int16)) | ((s == 0) & (d == 0))
+        assert bool(same.all())
+    ts = oracle_tensors(L)
+    flag = oracle_step(L, ts)
+    got = gl.download()
+    rep = compare(got, ts, label="producer overlap")
+    if w.with_flag:
+        assert got["flag"] == flag == 0
+    log(f"  {rep}")
+    gl.free()
+
+
 def test_range_with_fp16_gradients_and_copy():
     w = ragged(2, "fp16", grad_prescale=1024.0, unscale=1 / 1024)
     L = synth.make_layer(w)
@@ -367,3 +413,70 @@ def test_copy_reference_copies_exactly(units):
     if n >= 32:
         with pytest.raises(la.LayerAdamError, match="MISALIGNED"):
             la.copy_reference(big[8:8 + n - 16], src[:n - 16])
+
+
+# ---------------------------------------------------------------------------
+# The stream probe (measurement aid): the update's traffic, no arithmetic
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("out", ["bf16", "fp16", "none"])
+@pytest.mark.parametrize("R", [1, 2, 5, 8])
+def test_stream_probe_rewrites_state_and_xors_the_replicas(R, out):
+    w = ragged(R, seed=3900)
+    log(f"case probe R={R} out={out}")
+    L = synth.make_layer(w)
+    gl = GpuLayer(L, out=out)
+    la.stream_probe(gl.params, gl.grads)
+    got = gl.download()
+    for i in range(len(w.tensors)):
+        for field, want in (("master", L.master), ("exp_avg", L.exp_avg),
+                            ("exp_avg_sq", L.exp_avg_sq)):
+            assert np.array_equal(got[field][i].view(np.uint32), want[i].view(np.uint32)), \
+                (field, i)
+        x = L.grad(0, i).copy()
+        for r in range(1, R):
+            x ^= L.grad(r, i)
+        if out == "none":
+            assert np.all(got["weight_out"][i] == 0x7FAA)
+        else:
+            assert np.array_equal(got["weight_out"][i], x), i
+    assert got["flag"] == 0
+    # the next update rewrites the copy: one step equals the oracle's
+    gl.step()
+    ts = oracle_tensors(L)
+    oracle_step(L, ts, out=out)
+    compare(gl.download(), ts, label=f"after probe R={R}", out=out)
+    gl.free()
+
+
+def test_update_overlaps_gradients_arriving_over_the_host_link():
+    """Per-chunk release behind DMA: each chunk of every replica is copied from
+    pinned host memory on one stream; the update of that chunk waits on its
+    event on a second stream. Every element is compared with the oracle."""
+    w = synth.shrink(synth.WORKLOADS["qwen3_14b_layer"], 32)
+    log(f"case host-link producer {w.name}: N={w.numel} R={w.replicas}")
+    L = synth.make_layer(w)
+    gl = GpuLayer(L)
+    from synth.producer import HostLinkProducer, flat_to_layer
+    host = [torch.from_numpy(g.view(np.int16)).view(torch.bfloat16).pin_memory()
+            for g in L.grad_flat]
+    for g in gl.grad_flat:
+        g.zero_()
+    prod = HostLinkProducer(host, gl.grad_flat, chunk_elems=(1 << 20) + 8)
+    sizes = [n for _, n in w.tensors]
+    layer = la.Layer(gl.params, gl.grads)
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    side.wait_stream(main)
+    for c, (a, b) in enumerate(prod.bounds):
+        prod.produce(c)
+        ready = torch.cuda.Event()
+        ready.record(main)
+        side.wait_event(ready)
+        lo, hi = (flat_to_layer(L.grad_offsets, sizes, x) for x in (a, b))
+        layer.step_range(lo, hi, step=w.step, stream=side, **w.hyper)
+    main.wait_stream(side)
+    torch.cuda.synchronize()
+    assert len(prod.bounds) > 5
+    ts = oracle_tensors(L)
+    oracle_step(L, ts)
+    log(f"  {compare(gl.download(), ts, label='host-link overlap')}")
+    gl.free()
