@@ -35,7 +35,9 @@
 // layer. Loads carry the non-temporal hint (nothing is reused); stores are
 // written through the L2 to memory (buffer stores with the sc0, sc1 and nt
 // policy bits), which measured 1-8 % faster than non-temporal write-back
-// stores, the most where writes are the largest share of the traffic.
+// stores, the most where writes are the largest share of the traffic. Both
+// are buffer instructions on a resource built per chunk from the uniform
+// chunk base, so the per-lane offset is a 32-bit register.
 //
 // Arithmetic is IEEE binary32 with one rounding per operation: contraction
 // into fused multiply-adds is switched off for this file, and division and
@@ -80,9 +82,10 @@ namespace {
 // Update and probe: 1 issues their loads (stores) as buffer instructions
 // with the cache-policy bits LA_LOAD_CPOL (LA_STORE_CPOL) -- 1 = sc0,
 // 2 = nt, 16 = sc1 -- instead of global instructions with the non-temporal
-// hint. Stores default to sc0 | sc1 | nt: written through to memory.
+// hint. Loads default to nt, stores to sc0 | sc1 | nt: written through to
+// memory.
 #ifndef LA_BUFFER_LOADS
-#define LA_BUFFER_LOADS 0
+#define LA_BUFFER_LOADS 1
 #endif
 #ifndef LA_BUFFER_STORES
 #define LA_BUFFER_STORES 1
