@@ -615,6 +615,15 @@ def main():
             first["weight_out"].append(wb.view(torch.int16).cpu().numpy().view(np.uint16))
     flag_first = int(flag.item()) if flag is not None else None
 
+    # The stream probe (the update's bytes and launch shape, no arithmetic)
+    # and the reference copy, measured before the timed region: their 50+ ms
+    # of traffic over the same buffers also settle the memory system, which
+    # runs a fresh layer a few percent slower for its first tens of
+    # milliseconds. The probe leaves master, m and v unchanged; the next
+    # update rewrites the compute copy it overwrites.
+    probe = stream_probe(torch, layer, w)
+    copy_ref = copy_reference(torch, la)
+
     t = w.step + 1
     for _ in range(args.warmup):
         one_step(t)
@@ -673,8 +682,8 @@ def main():
                      "median_launch_ms": statistics.median(launch_ms),
                      "min_launch_ms": min(launch_ms), "max_launch_ms": max(launch_ms)},
         "overflow_flag_first_step": flag_first,
-        "stream_probe": stream_probe(torch, layer, w),
-        "hbm_copy_reference": copy_reference(torch, la),
+        "stream_probe": probe,
+        "hbm_copy_reference": copy_ref,
         "extras": None,
         "per_workload": None,
         "cpu_baseline": None,
