@@ -60,3 +60,35 @@ def test_host_resident_update_matches_the_oracle(where):
     want_flag = oracle_step(L, ts)
     log(f"  {compare(got, ts, label=where)}")
     assert got["flag"] == want_flag == 0
+
+
+def test_host_resident_update_at_size():
+    """The 14B layer's tensor shapes divided by 32 (10.3M parameters, R = 8,
+    1 % outliers): master, m and v in pinned host memory, gradients and the
+    compute copy in HBM, two consecutive steps; every element against the
+    oracle."""
+    w = synth.shrink(synth.WORKLOADS["qwen3_14b_layer"], 32)
+    assert w.numel > 10_000_000
+    log(f"case host-resident at size: N={w.numel} R={w.replicas}")
+    L = synth.make_layer(w)
+    params, grads = [], []
+    flat = [torch.from_numpy(g.view(np.int16)).cuda().view(torch.bfloat16) for g in L.grad_flat]
+    for i, (_, n) in enumerate(w.tensors):
+        params.append((pinned(L.master[i]), pinned(L.exp_avg[i]), pinned(L.exp_avg_sq[i]),
+                       torch.empty(n, dtype=torch.bfloat16, device="cuda")))
+        off = L.grad_offsets[i]
+        grads.append([g[off:off + n] for g in flat])
+    layer = la.Layer(params, grads)
+    ts = oracle_tensors(L)
+    for t in (w.step, w.step + 1):
+        layer.step(step=t, **w.hyper)
+        oracle_step(L, ts, t=t)
+    torch.cuda.synchronize()
+    got = {"master": [p.numpy().copy() for p, _, _, _ in params],
+           "exp_avg": [m.numpy().copy() for _, m, _, _ in params],
+           "exp_avg_sq": [v.numpy().copy() for _, _, v, _ in params],
+           "weight_out": [wb.view(torch.int16).cpu().numpy().view(np.uint16)
+                          for _, _, _, wb in params]}
+    rep = compare(got, ts, label="host-resident at size")
+    assert rep.compared == w.numel
+    log(f"  {rep}")
