@@ -45,6 +45,25 @@ def test_bench_prints_one_consistent_json_line():
     assert rf["min_launch_ms"] <= rf["mean_launch_ms"] <= rf["max_launch_ms"]
     assert rf["traffic"] is None or rf["traffic"] > 0
 
+    # the stream probe: the same bytes, measured on the same layer
+    sp = d["stream_probe"]
+    assert sp["gbs"] == pytest.approx(w.traffic_bytes / sp["ms"] / 1e6, rel=1e-9)
+    assert rf["frac_of_stream_probe"] == pytest.approx(rf["achieved"] / sp["gbs"], rel=1e-9)
+    assert 0.0 < sp["frac"] < 1.0
+
+    # every workload, each with the update and the probe
+    pw = d["per_workload"]
+    assert set(pw) == set(synth.WORKLOADS)
+    for name, e in pw.items():
+        ww = synth.WORKLOADS[name]
+        assert e["params"] == ww.numel and e["bytes_per_param"] == ww.bytes_per_param
+        for k in ("update", "probe"):
+            assert e[k]["gbs"] == pytest.approx(ww.traffic_bytes / e[k]["ms"] / 1e6, rel=1e-9)
+            assert e[k]["gparams"] == pytest.approx(ww.numel / e[k]["ms"] / 1e6, rel=1e-9)
+        if ww.with_flag:
+            assert e["overflow_flag"] == 0
+    assert "note" in pw["tiny"]
+
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] == 1 and cb["value"] > 0
     assert cb["unit"] == "Gparam/s" and cb["sample"]
