@@ -65,14 +65,6 @@ namespace {
 #ifndef LA_TILE_UNROLL
 #define LA_TILE_UNROLL 1
 #endif
-// With several tiles per chunk, the order of a chunk's loads (L), arithmetic
-// (C) and stores (S) per tile u, held by scheduling barriers: 0 = the
-// compiler's choice (no barriers); 1 = L0 L1 .. | C0 S0 | C1 S1 ..;
-// 2 = L0 L1 .. | C0 C1 .. | S0 S1 ..; 3 = L0 C0 S0 | L1 C1 S1 ..;
-// 4 = L0 C0 | L1 S0 C1 | L2 S1 C2 .. | S_last.
-#ifndef LA_SCHEDULE
-#define LA_SCHEDULE 0
-#endif
 #ifndef LA_NT_LOADS
 #define LA_NT_LOADS 1
 #endif
@@ -105,8 +97,8 @@ namespace {
 #define LA_WORKGROUPS_PER_CU -1
 #endif
 // The finite check only reads: more requests in flight help it (measured
-// 7.1 TB/s with 128-thread workgroups, 8 tiles per chunk and no residency
-// cap, against 5.5 TB/s with a residency cap of one wave per SIMD).
+// 6.8-7.1 TB/s with 128-thread workgroups, 8 tiles per chunk and no
+// residency cap, against 5.5 TB/s with a residency cap of one wave per SIMD).
 #ifndef LA_CHECK_BLOCK
 #define LA_CHECK_BLOCK 128      // finite check: threads per workgroup
 #endif
@@ -126,7 +118,6 @@ constexpr int kCheckBlock = LA_CHECK_BLOCK;
 constexpr int kCheckUnroll = LA_CHECK_TILE_UNROLL;
 constexpr int kCheckChunk = kCheckBlock * kVec * kCheckUnroll;
 static_assert(kVec == 4 || kVec == 8, "4 or 8 elements per thread per tile");
-static_assert(LA_SCHEDULE >= 0 && LA_SCHEDULE <= 4, "schedules 0 .. 4");
 static_assert(kBlock % 64 == 0 && kBlock <= 1024, "whole waves");
 static_assert(kCheckBlock % 64 == 0 && kCheckBlock <= 1024, "whole waves");
 static_assert(kChunk > kMaxUnalignedEntry && kCheckChunk > kMaxUnalignedEntry,
@@ -157,12 +148,19 @@ __device__ __forceinline__ void store_stream(T v, T* p) {
   else *p = v;
 }
 
+// Buffer resource over a uniform base pointer: no stride, a range far past
+// the one chunk the offsets address, and the fourth descriptor word of a raw
+// 32-bit-format buffer on this architecture (data format field = 32 bits).
+constexpr int kRsrcRange = 0x7fffffff;
+constexpr int kRsrcWord3 = 0x00020000;
+
 // T (16 or 8 bytes) at element `elem` of a uniform base pointer.
 template <typename T, typename E>
 __device__ __forceinline__ T load_at(const E* base, uint32_t elem) {
+  static_assert(sizeof(T) == 16 || sizeof(T) == 8, "16- or 8-byte accesses");
   if constexpr (LA_BUFFER_LOADS) {
     const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<E*>(base), 0, 0x7fffffff, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<E*>(base), 0, kRsrcRange, kRsrcWord3);
     const uint32_t byte = elem * static_cast<uint32_t>(sizeof(E));
     if constexpr (sizeof(T) == 16)
       return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, byte, 0, LA_LOAD_CPOL));
@@ -175,11 +173,12 @@ __device__ __forceinline__ T load_at(const E* base, uint32_t elem) {
 
 template <typename T, typename E>
 __device__ __forceinline__ void store_at(T x, E* base, uint32_t elem) {
+  static_assert(sizeof(T) == 16 || sizeof(T) == 8, "16- or 8-byte accesses");
   if constexpr (LA_BUFFER_STORES) {
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(base, 0, kRsrcRange, kRsrcWord3);
     const uint32_t byte = elem * static_cast<uint32_t>(sizeof(E));
     if constexpr (sizeof(T) == 16)
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, byte, 0,
@@ -458,68 +457,18 @@ layer_adam_kernel(const KernelArgs<R> a) {
     for (int r = 0; r < R; ++r) g[r] = T.g[r] + base;
 
     if (base + kChunk <= n) {
-      // Full chunk: loads, arithmetic and stores of every tile, in the
-      // order kSchedule names.
-      constexpr int kSchedule = LA_SCHEDULE;
+      // Full chunk: every load of the chunk, then per tile the arithmetic and
+      // the stores.
       TileRegs<R> x[kUnroll];
-      TileOut y[kUnroll];
-      auto load = [&](int u) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
         load_tile<R>(x[u], p, m, v, g, tile_offset<kBlock, kUnroll>(u, tid));
-      };
-      auto compute = [&](int u) {
-        if constexpr (MODE == kProbe) probe_tile<R, OUT>(x[u], a.key, y[u]);
-        else update_tile<R, FP16, FLAG, OUT>(x[u], s, bad, y[u]);
-      };
-      auto store = [&](int u) {
-        store_tile<OUT>(y[u], p, m, v, w, tile_offset<kBlock, kUnroll>(u, tid));
-      };
-      auto fence = [] {
-        if constexpr (kSchedule != 0) __builtin_amdgcn_sched_barrier(0);
-      };
-      if constexpr (kSchedule <= 2) {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) load(u);
-        fence();
-      }
-      if constexpr (kSchedule <= 1) {
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          compute(u);
-          fence();
-          store(u);
-          fence();
-        }
-      } else if constexpr (kSchedule == 2) {
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) compute(u);
-        fence();
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) store(u);
-      } else if constexpr (kSchedule == 3) {
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          load(u);
-          fence();
-          compute(u);
-          fence();
-          store(u);
-          fence();
-        }
-      } else {
-        load(0);
-        fence();
-        compute(0);
-        fence();
-#pragma unroll
-        for (int u = 1; u < kUnroll; ++u) {
-          load(u);
-          fence();
-          store(u - 1);
-          fence();
-          compute(u);
-          fence();
-        }
-        store(kUnroll - 1);
+      for (int u = 0; u < kUnroll; ++u) {
+        TileOut y;
+        if constexpr (MODE == kProbe) probe_tile<R, OUT>(x[u], a.key, y);
+        else update_tile<R, FP16, FLAG, OUT>(x[u], s, bad, y);
+        store_tile<OUT>(y, p, m, v, w, tile_offset<kBlock, kUnroll>(u, tid));
       }
     } else {
       // Last, partial chunk of a tensor: element by element, bounds-checked.
