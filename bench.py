@@ -21,6 +21,10 @@ Prints one JSON line:
   per_workload every workload in turn (inputs drawn, uploaded, timed, freed):
                mean launch time of the update and of the probe, Gparam/s,
                GB/s and fraction of 8 TB/s
+  extras       the neighbouring entry points on the same layer (chunked
+               range updates, finite check and gated step, other copy
+               formats, one GPU's shard, host-resident state) and the
+               per-chunk overlap of the update with two gradient producers
   cpu_baseline the CPU oracle timed on this host (one core) on a bounded
                prefix of the same layer, with its parity against the GPU's
                first step on that prefix
@@ -317,7 +321,6 @@ def stream_probe(torch, layer, w, reps=20):
 def per_workload(torch, la, synth, reps=20):
     """Every workload in turn: draw, upload, time the update and the probe
     (mean launch time over reps launches, HIP events), free."""
-    import numpy as np
     out = {}
     for name, w in synth.WORKLOADS.items():
         t_draw = time.time()
