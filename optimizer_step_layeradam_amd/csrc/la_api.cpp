@@ -483,6 +483,6 @@ LA_API int64_t la_traffic_bytes(const la_layer_desc* layer) {
 
 LA_API const char* la_last_error(void) { return g_error; }
 
-LA_API const char* la_version(void) { return "layeradam 0.3.0 gfx950"; }
+LA_API const char* la_version(void) { return "layeradam 0.4.0 gfx950"; }
 
 }  // extern "C"
