@@ -480,3 +480,23 @@ def test_update_overlaps_gradients_arriving_over_the_host_link():
     oracle_step(L, ts)
     log(f"  {compare(gl.download(), ts, label='host-link overlap')}")
     gl.free()
+
+
+def test_stream_probe_over_several_launches_with_empty_tensors():
+    """40 tensors (some empty) split into several launches: the probe leaves
+    every state element unchanged and writes the XOR copy of every element."""
+    sizes = [(f"t{k}", 0 if k % 7 == 3 else 1 + (k * 7919) % 20000) for k in range(40)]
+    w = synth.Workload(name="probe_forty", seed=3950, tensors=tuple(sizes), replicas=3,
+                       grad_dtype="bf16", step=2)
+    log(f"case probe forty tensors N={w.numel}")
+    L = synth.make_layer(w)
+    gl = GpuLayer(L)
+    la.Layer(gl.params, gl.grads).stream_probe()
+    got = gl.download()
+    for i, (_, n) in enumerate(w.tensors):
+        for field, want in (("master", L.master), ("exp_avg", L.exp_avg),
+                            ("exp_avg_sq", L.exp_avg_sq)):
+            assert np.array_equal(got[field][i].view(np.uint32), want[i].view(np.uint32))
+        x = L.grad(0, i) ^ L.grad(1, i) ^ L.grad(2, i)
+        assert np.array_equal(got["weight_out"][i], x), i
+    gl.free()
