@@ -228,9 +228,10 @@ LA_API la_status la_copy_reference(void *dst, const void *src, int64_t bytes,
  * until the next update rewrites it. Its rate is what HBM gives this mix of
  * R + 3 read and 4 write streams: the beta of the step-time bound
  * T >= max_j W_j / beta_j ("SlideDP", 研究动机 and 技术新颖性) measured for
- * the update's own access pattern. Arguments are checked as for
- * layer_adam_step (no hyperparameters; the gradient dtype does not matter);
- * nothing is enqueued on failure. */
+ * the update's own access pattern. Like an update, it rewrites the layer's
+ * state, so it must not overlap another call on the same buffers. Arguments
+ * are checked as for layer_adam_step (no hyperparameters; the gradient dtype
+ * does not matter); nothing is enqueued on failure. */
 LA_API la_status la_stream_probe(const la_layer_desc *layer, void *hip_stream);
 
 /* Bytes of mixed-precision Adam state the layer stands for: 16 per
