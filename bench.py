@@ -23,8 +23,10 @@ Prints one JSON line:
                GB/s and fraction of 8 TB/s
   extras       the neighbouring entry points on the same layer (chunked
                range updates, finite check and gated step, other copy
-               formats, one GPU's shard, host-resident state) and the
-               per-chunk overlap of the update with two gradient producers
+               formats, one GPU's shard, host-resident state), the
+               per-chunk overlap of the update with two gradient producers,
+               and the update's traffic split by direction (its loads alone,
+               its stores alone, in sequence, at once, alternating by slice)
   cpu_baseline the CPU oracle timed on this host (one core) on a bounded
                prefix of the same layer, with its parity against the GPU's
                first step on that prefix
@@ -448,6 +450,64 @@ def producer_overlap(torch, la, w, L, params, grads, flat, t0, k=1024, reps=3,
     return out
 
 
+def direction_split(torch, la, layer, w, update_ms, reps=10):
+    """The update's traffic taken apart by direction on the resident layer,
+    with the library's direction probe: its loads alone ((2R + 12) B/param),
+    its stores alone (14 B/param), the two in sequence, the two at once on
+    two streams, and the two alternating over P consecutive slices of the
+    layer (a read phase, then the write phase of the same slice), against the
+    update itself. The write part overwrites the state (with zeros), so this
+    runs after every measurement that needs it."""
+    n = w.numel
+    read_b = (2 * w.replicas + 12) * n
+    write_b = w.traffic_bytes - read_b
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+
+    def entry(ms, nbytes):
+        gbs = nbytes / ms / 1e6
+        return {"ms": ms, "gbs": gbs, "frac": gbs / PEAK_HBM_GBS}
+
+    def reads(lo=0, hi=n, stream=None):
+        layer.direction_probe(la.PROBE_READS, lo, hi, stream=stream)
+
+    def writes(lo=0, hi=n, stream=None):
+        layer.direction_probe(la.PROBE_WRITES, lo, hi, fill=0, stream=stream)
+
+    def at_once():
+        start = torch.cuda.Event()
+        start.record(main)
+        side.wait_event(start)
+        writes(stream=side)
+        reads()
+        done = torch.cuda.Event()
+        done.record(side)
+        main.wait_event(done)
+
+    r_ms = time_launches(torch, reads, reps=reps, warm=3, warm_ms=WARM_MS)
+    w_ms = time_launches(torch, writes, reps=reps, warm=3)
+    out = {"read_bytes_per_param": 2 * w.replicas + 12,
+           "write_bytes_per_param": w.bytes_per_param - 2 * w.replicas - 12,
+           "kernel": "direction_kernel (la_direction_probe)",
+           "reads_alone": entry(r_ms, read_b), "writes_alone": entry(w_ms, write_b),
+           "in_sequence": entry(r_ms + w_ms, w.traffic_bytes),
+           "at_once_two_streams": entry(time_launches(torch, at_once, reps=reps, warm=2),
+                                        w.traffic_bytes),
+           "update": entry(update_ms, w.traffic_bytes)}
+    phases = {}
+    for p in (1, 4, 16, 64):
+        cuts = [n * k // p for k in range(p + 1)]
+
+        def alternate():
+            for lo, hi in zip(cuts, cuts[1:]):
+                reads(lo, hi)
+                writes(lo, hi)
+
+        phases[str(p)] = dict(entry(time_launches(torch, alternate, reps=5, warm=2),
+                                    w.traffic_bytes), params_per_phase=n // p)
+    out["alternating_phases"] = phases
+    return out
+
+
 def extras(torch, la, w, params, grads, t0):
     """The neighbouring entry points on the same resident layer, timed after
     the main region: the layer released in 64 MiB gradient chunks through the
@@ -702,6 +762,8 @@ def main():
         log("bench: producer overlap")
         out["extras"]["producer_overlap"] = producer_overlap(torch, la, w, L, params, grads,
                                                              _flat, t + 1000)
+        log("bench: direction split")
+        out["extras"]["direction_split"] = direction_split(torch, la, layer, w, mean_ms)
     del layer, params, grads, _flat
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

@@ -234,6 +234,32 @@ LA_API la_status la_copy_reference(void *dst, const void *src, int64_t bytes,
  * does not matter); nothing is enqueued on failure. */
 LA_API la_status la_stream_probe(const la_layer_desc *layer, void *hip_stream);
 
+/* Parts of the direction probe. */
+typedef enum { LA_PROBE_READS = 0, LA_PROBE_WRITES = 1 } la_probe_part;
+
+/* Measurement aid, not part of the update: the stream probe split by
+ * direction, over the layer's elements [elem_begin, elem_end) (numbering as
+ * in la_layer_desc). LA_PROBE_READS issues exactly the loads an update of
+ * that range issues -- the R gradient replicas, master, m and v, in the
+ * update's per-wave pattern (one 64-lane wave per 256-element chunk) -- and
+ * writes nothing. LA_PROBE_WRITES issues exactly its stores -- master, m and
+ * v (each element the 32-bit pattern `fill`) and the compute copy (the low
+ * 16 bits of `fill`; nothing with LA_OUT_NONE) -- and reads nothing, so it
+ * overwrites the layer's state in the range. Timed alone, one after the
+ * other, at once on two streams, or alternating over slices of the layer,
+ * the two parts show the bandwidth HBM gives each direction of the update's
+ * traffic and what interleaving the two directions costs: the per-resource
+ * beta of the step-time bound T >= max_j W_j / beta_j ("SlideDP", 研究动机
+ * and 技术新颖性) taken apart for HBM. workgroups_per_cu: resident one-wave
+ * workgroups per compute unit, 1..64, 0 for no cap, -1 for the part's
+ * default. Arguments are checked as for la_stream_probe, plus the part, the
+ * residency and the range; nothing is enqueued on failure. Must not overlap
+ * another call on the same buffers. */
+LA_API la_status la_direction_probe(const la_layer_desc *layer, int32_t part,
+                                    int64_t elem_begin, int64_t elem_end,
+                                    uint32_t fill, int32_t workgroups_per_cu,
+                                    void *hip_stream);
+
 /* Bytes of mixed-precision Adam state the layer stands for: 16 per
  * parameter (2 BF16 weight + 2 gradient + 4 FP32 master + 8 FP32 m and v).
  * -1 if the descriptor is invalid. Host only. */

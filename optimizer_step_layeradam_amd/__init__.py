@@ -27,11 +27,12 @@ STATUS_NAMES = {0: "LA_OK", 1: "LA_ERR_INVALID_ARGUMENT", 2: "LA_ERR_MISALIGNED"
                 3: "LA_ERR_ALIASING", 4: "LA_ERR_UNSUPPORTED", 5: "LA_ERR_HIP"}
 GRAD_BF16, GRAD_FP16 = 0, 1
 OUT_BF16, OUT_FP16, OUT_NONE = 0, 1, 2
+PROBE_READS, PROBE_WRITES = 0, 1
 
 # Exported symbols, as declared in include/layeradam.h.
 EXPORTS = ("layer_adam_step", "layer_adam_step_range", "layer_adam_step_gated",
            "layer_adam_step_device_step", "la_check_gradients", "la_stream_probe",
-           "la_copy_reference",
+           "la_direction_probe", "la_copy_reference",
            "la_state_bytes", "la_traffic_bytes", "la_last_error", "la_version")
 
 
@@ -168,6 +169,10 @@ def load(path: Optional[str] = None):
     lib.la_check_gradients.restype = ctypes.c_int
     lib.la_stream_probe.argtypes = [ctypes.POINTER(LayerDesc), ctypes.c_void_p]
     lib.la_stream_probe.restype = ctypes.c_int
+    lib.la_direction_probe.argtypes = [ctypes.POINTER(LayerDesc), ctypes.c_int32, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_uint32, ctypes.c_int32,
+                                       ctypes.c_void_p]
+    lib.la_direction_probe.restype = ctypes.c_int
     lib.la_copy_reference.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                       ctypes.c_void_p]
     lib.la_copy_reference.restype = ctypes.c_int
@@ -270,6 +275,15 @@ def stream_probe_raw(desc: LayerDesc, stream: int = 0) -> None:
     """la_stream_probe on raw descriptors."""
     lib = load()
     _raise_on(lib.la_stream_probe(ctypes.byref(desc), stream or None), lib)
+
+
+def direction_probe_raw(desc: LayerDesc, part: int, begin: int, end: int, fill: int = 0,
+                        workgroups_per_cu: int = -1, stream: int = 0) -> None:
+    """la_direction_probe on raw descriptors."""
+    lib = load()
+    _raise_on(lib.la_direction_probe(ctypes.byref(desc), int(part), int(begin), int(end),
+                                     int(fill) & 0xFFFFFFFF, int(workgroups_per_cu),
+                                     stream or None), lib)
 
 
 def state_bytes_raw(desc: LayerDesc) -> int:
@@ -445,6 +459,20 @@ def stream_probe(params, grads, *, stream=None) -> None:
     del keep
 
 
+def direction_probe(params, grads, part: int, begin: int = 0, end: Optional[int] = None, *,
+                    fill: int = 0, workgroups_per_cu: int = -1, stream=None) -> None:
+    """la_direction_probe over the layer's elements [begin, end) (default: all):
+    PROBE_READS issues the update's loads only, PROBE_WRITES its stores only
+    (master, m, v set to the 32-bit pattern ``fill``, the compute copy to its
+    low 16 bits) -- a bandwidth measurement that overwrites the state."""
+    tensors, R, gd, od = _describe(params, grads)
+    desc, keep = make_layer(tensors, R, gd, od)
+    n = sum(t["numel"] for t in tensors)
+    direction_probe_raw(desc, part, begin, n if end is None else end, fill, workgroups_per_cu,
+                        _stream_ptr(stream))
+    del keep
+
+
 def check_gradients(grads, found_nonfinite, *, grad_unscale: float = 1.0, stream=None) -> None:
     """Set the int32 CUDA scalar ``found_nonfinite`` to 1 if some aggregated
     gradient (sum of the replicas times grad_unscale) is non-finite.
@@ -503,6 +531,11 @@ class Layer:
 
     def stream_probe(self, stream=None) -> None:
         stream_probe_raw(self._desc, _stream_ptr(stream))
+
+    def direction_probe(self, part: int, begin: int = 0, end: Optional[int] = None, *,
+                        fill: int = 0, workgroups_per_cu: int = -1, stream=None) -> None:
+        direction_probe_raw(self._desc, part, begin, self.numel if end is None else end, fill,
+                            workgroups_per_cu, _stream_ptr(stream))
 
     def state_bytes(self) -> int:
         return state_bytes_raw(self._desc)

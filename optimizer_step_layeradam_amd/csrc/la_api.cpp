@@ -91,8 +91,10 @@ bool finite_nonneg(double x) { return std::isfinite(x) && x >= 0.0; }
 bool aligned(const void* p, uintptr_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
 // kUpdate: the update (state and copy written); kProbe: the stream probe
-// (the same buffers, no arithmetic); kCheck: gradients read only.
-enum class Mode { kUpdate, kProbe, kCheck };
+// (the same buffers, no arithmetic); kCheck: gradients read only;
+// kReadProbe / kWriteProbe: the two parts of the direction probe (the
+// update's loads only, its stores only; checked as the stream probe).
+enum class Mode { kUpdate, kProbe, kCheck, kReadProbe, kWriteProbe };
 
 // Counts, dtypes and sizes; no pointers (enough for the byte accounting).
 la_status check_counts(const la_layer_desc* layer) {
@@ -269,9 +271,12 @@ int64_t total_numel(const la_layer_desc* layer) {
 // the next multiple of 8 (at most 7 elements, so always the element-wise
 // path of the kernel) becomes its own entry, and the rest starts 16-byte
 // aligned (32 bytes into FP32 arrays, 16 into 16-bit arrays).
+// fill and wg_per_cu serve the direction probe only (its stored pattern, and
+// its residency: -1 for the default).
 la_status enqueue(const la_layer_desc* layer, Mode mode, const la::Scalars& s,
                   const la::DeviceStep& dstep, int64_t begin, int64_t end, int32_t* flag,
-                  const int32_t* skip, void* hip_stream) {
+                  const int32_t* skip, void* hip_stream, uint32_t fill = 0,
+                  int wg_per_cu = -1) {
   la::TensorArgs batch[la::kTensorsPerLaunch];
   int pending = 0;
   int launches = 0;
@@ -290,7 +295,7 @@ la_status enqueue(const la_layer_desc* layer, Mode mode, const la::Scalars& s,
         return fail(LA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
       shape.grid_cap = kMaxGrid;
       device_facts(device, &shape.lds_per_cu, &shape.lds_per_block);
-      shape.wg_per_cu = workgroups_per_cu_override();
+      shape.wg_per_cu = wg_per_cu >= 0 ? wg_per_cu : workgroups_per_cu_override();
     }
     hipError_t e;
     switch (mode) {
@@ -301,6 +306,12 @@ la_status enqueue(const la_layer_desc* layer, Mode mode, const la::Scalars& s,
       case Mode::kProbe:
         e = la::launch_stream_probe(batch, pending, layer->num_replicas, layer->out_dtype,
                                     stream, shape);
+        break;
+      case Mode::kReadProbe:
+      case Mode::kWriteProbe:
+        e = la::launch_direction_probe(
+            batch, pending, layer->num_replicas, layer->out_dtype,
+            mode == Mode::kReadProbe ? la::kProbeReads : la::kProbeWrites, fill, stream, shape);
         break;
       default:
         e = la::launch_check_gradients(batch, pending, layer->num_replicas, fp16, s.u, flag,
@@ -442,6 +453,29 @@ LA_API la_status la_stream_probe(const la_layer_desc* layer, void* hip_stream) {
                  total_numel(layer), nullptr, nullptr, hip_stream);
 }
 
+LA_API la_status la_direction_probe(const la_layer_desc* layer, int32_t part,
+                                    int64_t elem_begin, int64_t elem_end, uint32_t fill,
+                                    int32_t workgroups_per_cu, void* hip_stream) {
+  la_status st = check_counts(layer);
+  if (st != LA_OK) return st;
+  if ((st = check_pointers(layer, Mode::kProbe)) != LA_OK) return st;
+  if (part != LA_PROBE_READS && part != LA_PROBE_WRITES)
+    return fail(LA_ERR_INVALID_ARGUMENT, "part = %d, need LA_PROBE_READS or LA_PROBE_WRITES",
+                part);
+  if (workgroups_per_cu < -1 || workgroups_per_cu > 64)
+    return fail(LA_ERR_INVALID_ARGUMENT, "workgroups_per_cu = %d, need -1..64",
+                workgroups_per_cu);
+  const int64_t n = total_numel(layer);
+  if (elem_begin < 0 || elem_begin > elem_end || elem_end > n)
+    return fail(LA_ERR_INVALID_ARGUMENT, "element range [%lld, %lld) outside [0, %lld]",
+                static_cast<long long>(elem_begin), static_cast<long long>(elem_end),
+                static_cast<long long>(n));
+  if ((st = check_aliasing(layer, Mode::kProbe, nullptr, nullptr)) != LA_OK) return st;
+  return enqueue(layer, part == LA_PROBE_READS ? Mode::kReadProbe : Mode::kWriteProbe,
+                 la::Scalars{}, la::DeviceStep{nullptr, 0.0, 0.0, 0.0}, elem_begin, elem_end,
+                 nullptr, nullptr, hip_stream, fill, workgroups_per_cu);
+}
+
 LA_API la_status la_copy_reference(void* dst, const void* src, int64_t bytes,
                                    void* hip_stream) {
   if (bytes < 0 || bytes % 16 != 0)
@@ -483,6 +517,6 @@ LA_API int64_t la_traffic_bytes(const la_layer_desc* layer) {
 
 LA_API const char* la_last_error(void) { return g_error; }
 
-LA_API const char* la_version(void) { return "layeradam 0.4.0 gfx950"; }
+LA_API const char* la_version(void) { return "layeradam 0.5.0 gfx950"; }
 
 }  // extern "C"

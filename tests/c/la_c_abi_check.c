@@ -1,8 +1,8 @@
 /*
  * la_c_abi_check.c -- the C ABI used from plain C, without Python or torch:
  * device buffers from hipMalloc, inputs drawn by the seeded generator
- * (libla_synth.so), the stream probe and then one layer_adam_step on a side
- * stream, results compared
+ * (libla_synth.so), the stream probe and the read part of the direction
+ * probe, then one layer_adam_step on a side stream, results compared
  * element by element with the CPU oracle (libla_oracle.so). Test program;
  * exit status 0 when every master/m/v element is within 2 FP32 ulp of the
  * oracle (0 expected) and every BF16 element is identical.
@@ -97,10 +97,18 @@ int main(void) {
   printf("%s; state %lld B, traffic %lld B\n", la_version(),
          (long long)la_state_bytes(&layer), (long long)la_traffic_bytes(&layer));
   /* the stream probe moves the update's bytes and leaves the state as it
-     was: the step after it must still match the oracle */
+     was, and the read part of the direction probe only reads: the step after
+     them must still match the oracle */
   la_status st = la_stream_probe(&layer, stream);
   if (st != LA_OK) {
     fprintf(stderr, "la_stream_probe: %d %s\n", st, la_last_error());
+    return 2;
+  }
+  int64_t total = 0;
+  for (int t = 0; t < NT; ++t) total += numel[t];
+  st = la_direction_probe(&layer, LA_PROBE_READS, 0, total, 0u, -1, stream);
+  if (st != LA_OK) {
+    fprintf(stderr, "la_direction_probe: %d %s\n", st, la_last_error());
     return 2;
   }
   st = layer_adam_step(&layer, &hyper, flag, stream);

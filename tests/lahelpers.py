@@ -24,10 +24,11 @@ ULP_TOL = 2
 
 
 # Tensor sizes of the ragged layers: single elements, the short entries that
-# may start unaligned, both sides of the update's 512-element chunk and of the
-# 2048- and 4096-element powers of two (the finite check's chunk), and
-# longer tensors with ragged tails.
-RAGGED = (("a", 1), ("b", 3), ("c", 7), ("j", 511), ("k", 512), ("l", 513),
+# may start unaligned, both sides of the update's 256-element chunk and of
+# two chunks, of the 2048- and 4096-element powers of two (4096: the finite
+# check's chunk), and longer tensors with ragged tails.
+RAGGED = (("a", 1), ("b", 3), ("c", 7), ("p", 255), ("q", 256), ("r", 257),
+          ("j", 511), ("k", 512), ("l", 513),
           ("d", 2047), ("e", 2048), ("f", 2049), ("m", 4095), ("n", 4096), ("o", 4097),
           ("g", 4101), ("h", 10001), ("i", 65536 + 13))
 

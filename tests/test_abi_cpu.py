@@ -407,3 +407,56 @@ def test_stream_probe_of_an_empty_layer_enqueues_nothing():
     desc, keep = la.make_layer([dict(numel=0)], 2, la.GRAD_BF16)
     la.stream_probe_raw(desc)
     assert la.last_error() == ""
+
+
+@host_only
+@pytest.mark.parametrize("case", ["bad_part", "wg_low", "wg_high", "range_past_end",
+                                  "range_reversed", "range_negative", "null_master",
+                                  "misaligned_m", "grad_on_v", "R0"])
+def test_direction_probe_refusals(case):
+    """The direction probe checks its buffers as the stream probe does, plus
+    its part, residency and element range; nothing is enqueued on a refusal."""
+    t, R = fake_tensor(0), 2
+    part, lo, hi, wg = la.PROBE_READS, 0, t["numel"], -1
+    if case == "bad_part":
+        part = 2
+    elif case == "wg_low":
+        wg = -2
+    elif case == "wg_high":
+        wg = 65
+    elif case == "range_past_end":
+        hi = t["numel"] + 1
+    elif case == "range_reversed":
+        lo, hi = 8, 4
+    elif case == "range_negative":
+        lo = -1
+    elif case == "null_master":
+        t["master"] = 0
+    elif case == "misaligned_m":
+        t["exp_avg"] += 8
+    elif case == "grad_on_v":
+        t["grads"][1] = t["exp_avg_sq"] + 64
+    elif case == "R0":
+        R = 0
+    desc, keep = la.make_layer([t], R, la.GRAD_BF16)
+    with pytest.raises(la.LayerAdamError) as e:
+        la.direction_probe_raw(desc, part, lo, hi, workgroups_per_cu=wg)
+    assert e.value.status == {"null_master": 1, "misaligned_m": 2, "grad_on_v": 3}.get(case, 1)
+    assert la.last_error()
+
+
+@pytest.mark.parametrize("part", [0, 1])
+def test_direction_probe_of_an_empty_layer_enqueues_nothing(part):
+    desc, keep = la.make_layer([dict(numel=0)], 2, la.GRAD_BF16)
+    la.direction_probe_raw(desc, part, 0, 0)
+    assert la.last_error() == ""
+
+
+@host_only
+@pytest.mark.parametrize("part", [0, 1])
+def test_direction_probe_of_an_empty_range_enqueues_nothing(part):
+    """An empty range of a non-empty layer launches nothing, so it succeeds
+    without a GPU."""
+    desc, keep = la.make_layer([fake_tensor(0)], 2, la.GRAD_BF16)
+    la.direction_probe_raw(desc, part, 40, 40)
+    assert la.last_error() == ""

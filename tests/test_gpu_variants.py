@@ -500,3 +500,93 @@ def test_stream_probe_over_several_launches_with_empty_tensors():
         x = L.grad(0, i) ^ L.grad(1, i) ^ L.grad(2, i)
         assert np.array_equal(got["weight_out"][i], x), i
     gl.free()
+
+
+# ---------------------------------------------------------------------------
+# The direction probe (the update's loads only, its stores only)
+# ---------------------------------------------------------------------------
+def _grads_unchanged(gl, L):
+    for gf, want in zip(gl.grad_flat, L.grad_flat):
+        assert np.array_equal(gf.view(torch.int16).cpu().numpy().view(np.uint16), want)
+
+
+@pytest.mark.parametrize("R", [1, 3, 8])
+def test_direction_probe_reads_change_nothing(R):
+    """The read part, at its default, uncapped and capped residency, over the
+    whole layer and over a range that starts unaligned: no state, copy,
+    gradient or flag changes."""
+    w = ragged(R, seed=4000)
+    log(f"case direction reads R={R}")
+    L = synth.make_layer(w)
+    gl = GpuLayer(L)
+    layer = la.Layer(gl.params, gl.grads)
+    for wg in (-1, 0, 3):
+        layer.direction_probe(la.PROBE_READS, workgroups_per_cu=wg)
+    layer.direction_probe(la.PROBE_READS, 5, w.numel - 3)
+    got = gl.download()
+    for i in range(len(w.tensors)):
+        for field, want in (("master", L.master), ("exp_avg", L.exp_avg),
+                            ("exp_avg_sq", L.exp_avg_sq)):
+            assert np.array_equal(got[field][i].view(np.uint32), want[i].view(np.uint32))
+        assert np.all(got["weight_out"][i] == 0x7FAA), i
+    assert got["flag"] == 0
+    _grads_unchanged(gl, L)
+    gl.free()
+
+
+@pytest.mark.parametrize("out", ["bf16", "none"])
+def test_direction_probe_writes_exactly_the_range(out):
+    """The write part over ranges that start and end inside tensors, at
+    unaligned elements, across tensor boundaries, and empty: every element in
+    a range holds the pattern (the copy its low half), every other element is
+    untouched, and no gradient changes."""
+    w = ragged(2, seed=4100)
+    log(f"case direction writes out={out}")
+    L = synth.make_layer(w)
+    gl = GpuLayer(L, out=out)
+    layer = la.Layer(gl.params, gl.grads)
+    bounds = np.cumsum([0] + [n for _, n in w.tensors])
+    want = {f: np.concatenate([a.view(np.uint32) for a in getattr(L, f)])
+            for f in ("master", "exp_avg", "exp_avg_sq")}
+    want_w = np.full(w.numel, 0x7FAA, np.uint16)
+    cases = [(3, 260, 0x11111111), (bounds[5] - 1, bounds[9] + 5, 0xA5A5C3C3),
+             (bounds[12] + 7, bounds[12] + 7, 0x22222222), (bounds[13] + 1, w.numel - 2, 0x3C003C00),
+             (0, 1, 0xFFFF0001)]
+    for k, (lo, hi, fill) in enumerate(cases):
+        layer.direction_probe(la.PROBE_WRITES, int(lo), int(hi), fill=fill,
+                              workgroups_per_cu=(-1, 0, 5)[k % 3])
+        for f in want:
+            want[f][lo:hi] = fill
+        if out != "none":
+            want_w[lo:hi] = fill & 0xFFFF
+    got = gl.download()
+    for f in want:
+        assert np.array_equal(np.concatenate([a.view(np.uint32) for a in got[f]]), want[f]), f
+    assert np.array_equal(np.concatenate(got["weight_out"]), want_w)
+    assert got["flag"] == 0
+    _grads_unchanged(gl, L)
+    gl.free()
+
+
+def test_direction_probe_over_several_launches_with_empty_tensors():
+    """40 tensors (some empty) split into several launches: the read part
+    changes nothing, the write part sets every element."""
+    sizes = [(f"t{k}", 0 if k % 7 == 3 else 1 + (k * 7919) % 20000) for k in range(40)]
+    w = synth.Workload(name="direction_forty", seed=4150, tensors=tuple(sizes), replicas=5,
+                       grad_dtype="fp16", step=2)
+    log(f"case direction forty tensors N={w.numel}")
+    L = synth.make_layer(w)
+    gl = GpuLayer(L, out="fp16")
+    layer = la.Layer(gl.params, gl.grads)
+    layer.direction_probe(la.PROBE_READS)
+    got = gl.download()
+    for i in range(len(w.tensors)):
+        assert np.array_equal(got["master"][i].view(np.uint32), L.master[i].view(np.uint32))
+    layer.direction_probe(la.PROBE_WRITES, fill=0x40490FDB)
+    got = gl.download()
+    for i in range(len(w.tensors)):
+        for f in ("master", "exp_avg", "exp_avg_sq"):
+            assert np.all(got[f][i].view(np.uint32) == 0x40490FDB), (f, i)
+        assert np.all(got["weight_out"][i] == 0x0FDB), i
+    _grads_unchanged(gl, L)
+    gl.free()

@@ -88,6 +88,10 @@ many[200]["exp_avg"] = many[17]["weight_out"] + 64 if many[17]["numel"] > 64 els
 d, k = la.make_layer(many, 2, 0)
 refused(lib.layer_adam_step(ctypes.byref(d), ctypes.byref(hp), None, None))
 assert lib.la_state_bytes(ctypes.byref(d)) > 0 and lib.la_traffic_bytes(ctypes.byref(d)) > 0
+# the direction probe: bad part, residency and range
+for part, lo, hi, wg in ((2, 0, 1024, -1), (0, 0, 1024, 65), (1, 0, 1024, -2), (0, 9, 3, -1),
+                         (1, 0, 1 << 40, -1)):
+    refused(lib.la_direction_probe(ctypes.byref(d), part, lo, hi, 0, wg, None))
 # the reference copy: odd size, NULL, misaligned, overlapping
 for dst, src, n in ((BASE, BASE + 0x10000000, 24), (0, BASE, 1024), (BASE + 8, BASE + 0x10000000, 1024),
                     (BASE, BASE + 512, 1024)):
