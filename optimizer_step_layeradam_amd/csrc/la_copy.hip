@@ -94,10 +94,11 @@ copy_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src, int64_t n16)
 #pragma unroll
       for (int u = 0; u < kCopyTiles; ++u) store_unit(r[u], dst + base, unit_offset(u, tid));
     } else {
+      // Last, partial chunk: unit by unit, bounds-checked, same cache policies.
 #pragma unroll 1
       for (int u = 0; u < kCopyTiles; ++u) {
-        const int64_t i = base + int64_t(u) * kCopyBlock + tid;
-        if (i < n16) dst[i] = src[i];
+        const int64_t k = int64_t(u) * kCopyBlock + tid;
+        if (base + k < n16) store_unit(__builtin_nontemporal_load(src + base + k), dst + base, k);
       }
     }
   }
