@@ -207,6 +207,41 @@ LA_API la_status layer_adam_step_device_step(const la_layer_desc *layer,
                                              int32_t *overflow_flag,
                                              void *hip_stream);
 
+/* Options of layer_adam_step_ex. A zero-initialised struct means the whole
+ * layer, t from hp->step, no overflow flag and no skip flag. */
+typedef struct {
+  int32_t use_range;               /* 0: the whole layer; 1: the elements
+                                      [elem_begin, elem_end), as for
+                                      layer_adam_step_range               */
+  int64_t elem_begin;
+  int64_t elem_end;
+  int32_t *overflow_flag;          /* as for layer_adam_step; NULL: none   */
+  const int32_t *skip_if_nonzero;  /* as for layer_adam_step_gated; NULL:
+                                      never skipped                        */
+  const int64_t *step_on_device;   /* as for layer_adam_step_device_step
+                                      (hp->step ignored); NULL: hp->step   */
+} la_step_options;
+
+/* layer_adam_step with any combination of the options above in one call:
+ * an element range (the per-chunk release of "SlideDP", 核心方法 and
+ * 方法步骤详情), the overflow flag, the device skip flag of the gated step
+ * (the loss-scaling reading of the FP16-gradient state of "SlideDP",
+ * 前置知识, described at la_check_gradients) and the step count read from
+ * device memory. Each option means exactly what it means for its own entry
+ * point. Together they make a whole overflow-gated step of a layer
+ * capturable in a HIP graph: la_check_gradients into a cleared flag, this
+ * call with that flag as skip_if_nonzero and a device step count, then the
+ * caller's own device-side increment of t when the flag is clear -- every
+ * replay then applies the next step, or skips it, with no host
+ * synchronisation. A launch whose skip flag is set reads nothing else (not
+ * even the step count). opts NULL: all defaults. Arguments are checked as
+ * for the entry points whose options are used, plus use_range (0 or 1);
+ * nothing is enqueued on failure. */
+LA_API la_status layer_adam_step_ex(const la_layer_desc *layer,
+                                    const la_adam_params *hp,
+                                    const la_step_options *opts,
+                                    void *hip_stream);
+
 /* Measurement aid, not part of the update: enqueue a plain copy of `bytes`
  * bytes from src to dst on `hip_stream`, with the update kernel's access
  * style (16-byte non-temporal loads and stores, one workgroup per chunk) but

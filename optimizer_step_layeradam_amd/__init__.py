@@ -31,7 +31,8 @@ PROBE_READS, PROBE_WRITES = 0, 1
 
 # Exported symbols, as declared in include/layeradam.h.
 EXPORTS = ("layer_adam_step", "layer_adam_step_range", "layer_adam_step_gated",
-           "layer_adam_step_device_step", "la_check_gradients", "la_stream_probe",
+           "layer_adam_step_device_step", "layer_adam_step_ex", "la_check_gradients",
+           "la_stream_probe",
            "la_direction_probe", "la_copy_reference",
            "la_state_bytes", "la_traffic_bytes", "la_last_error", "la_version")
 
@@ -61,6 +62,15 @@ class AdamParams(ctypes.Structure):
                 ("weight_decay", ctypes.c_double),
                 ("step", ctypes.c_int64),
                 ("grad_unscale", ctypes.c_double)]
+
+
+class StepOptions(ctypes.Structure):
+    _fields_ = [("use_range", ctypes.c_int32),
+                ("elem_begin", ctypes.c_int64),
+                ("elem_end", ctypes.c_int64),
+                ("overflow_flag", ctypes.c_void_p),
+                ("skip_if_nonzero", ctypes.c_void_p),
+                ("step_on_device", ctypes.c_void_p)]
 
 
 class LayerAdamError(RuntimeError):
@@ -164,6 +174,9 @@ def load(path: Optional[str] = None):
                                                 ctypes.POINTER(AdamParams), ctypes.c_void_p,
                                                 ctypes.c_void_p, ctypes.c_void_p]
     lib.layer_adam_step_device_step.restype = ctypes.c_int
+    lib.layer_adam_step_ex.argtypes = [ctypes.POINTER(LayerDesc), ctypes.POINTER(AdamParams),
+                                       ctypes.POINTER(StepOptions), ctypes.c_void_p]
+    lib.layer_adam_step_ex.restype = ctypes.c_int
     lib.la_check_gradients.argtypes = [ctypes.POINTER(LayerDesc), ctypes.c_double,
                                        ctypes.c_void_p, ctypes.c_void_p]
     lib.la_check_gradients.restype = ctypes.c_int
@@ -261,6 +274,21 @@ def step_device_step_raw(desc: LayerDesc, params: AdamParams, step_on_device: in
     _raise_on(lib.layer_adam_step_device_step(ctypes.byref(desc), ctypes.byref(params),
                                               step_on_device or None, overflow_flag or None,
                                               stream or None), lib)
+
+
+def step_ex_raw(desc: LayerDesc, params: AdamParams, begin: Optional[int] = None,
+                end: Optional[int] = None, overflow_flag: int = 0, skip_if_nonzero: int = 0,
+                step_on_device: int = 0, stream: int = 0) -> None:
+    """layer_adam_step_ex on raw descriptors: the element range [begin, end)
+    when both are given, else the whole layer; zero pointers mean no flag, no
+    skip flag and t from params.step."""
+    if (begin is None) != (end is None):
+        raise ValueError("give both begin and end, or neither")
+    opts = StepOptions(0 if begin is None else 1, int(begin or 0), int(end or 0),
+                       overflow_flag or None, skip_if_nonzero or None, step_on_device or None)
+    lib = load()
+    _raise_on(lib.layer_adam_step_ex(ctypes.byref(desc), ctypes.byref(params),
+                                     ctypes.byref(opts), stream or None), lib)
 
 
 def check_gradients_raw(desc: LayerDesc, grad_unscale: float, found_nonfinite: int,
@@ -449,6 +477,31 @@ def step_device_step(params, grads, step_on_device, *, lr: float, beta1: float, 
     del keep
 
 
+def step_ex(params, grads, begin: Optional[int] = None, end: Optional[int] = None, *,
+            lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
+            step: Optional[int] = None, grad_unscale: float = 1.0, overflow_flag=None,
+            skip_if_nonzero=None, step_on_device=None, stream=None) -> None:
+    """layer_adam_step_ex: the update with any combination of an element range
+    [begin, end), the overflow flag, a device skip flag (int32 CUDA scalar,
+    as for step_gated) and a device step count (int64 CUDA scalar, as for
+    step_device_step; then ``step`` is not used)."""
+    tensors, R, gd, od = _describe(params, grads)
+    desc, keep = make_layer(tensors, R, gd, od)
+    step_ex_raw(desc, _ex_params(lr, beta1, beta2, eps, weight_decay, step, grad_unscale,
+                                 step_on_device),
+                begin, end, _flag_ptr(overflow_flag),
+                _flag_ptr(skip_if_nonzero, "skip_if_nonzero"),
+                0 if step_on_device is None else _step_ptr(step_on_device), _stream_ptr(stream))
+    del keep
+
+
+def _ex_params(lr, beta1, beta2, eps, weight_decay, step, grad_unscale, step_on_device):
+    if step is None and step_on_device is None:
+        raise ValueError("give step, or step_on_device")
+    return make_params(lr, beta1, beta2, eps, weight_decay, 1 if step is None else step,
+                       grad_unscale)
+
+
 def stream_probe(params, grads, *, stream=None) -> None:
     """la_stream_probe: the update's loads, stores and launch shape without
     its arithmetic (master, m, v rewritten unchanged; the compute copy
@@ -523,6 +576,18 @@ class Layer:
                              make_params(lr, beta1, beta2, eps, weight_decay, 1, grad_unscale),
                              _step_ptr(step_on_device), _flag_ptr(overflow_flag),
                              _stream_ptr(stream))
+
+    def step_ex(self, begin: Optional[int] = None, end: Optional[int] = None, *, lr: float,
+                beta1: float, beta2: float, eps: float, weight_decay: float,
+                step: Optional[int] = None, grad_unscale: float = 1.0, overflow_flag=None,
+                skip_if_nonzero=None, step_on_device=None, stream=None) -> None:
+        step_ex_raw(self._desc,
+                    _ex_params(lr, beta1, beta2, eps, weight_decay, step, grad_unscale,
+                               step_on_device),
+                    begin, end, _flag_ptr(overflow_flag),
+                    _flag_ptr(skip_if_nonzero, "skip_if_nonzero"),
+                    0 if step_on_device is None else _step_ptr(step_on_device),
+                    _stream_ptr(stream))
 
     def check_gradients(self, found_nonfinite, *, grad_unscale: float = 1.0,
                         stream=None) -> None:

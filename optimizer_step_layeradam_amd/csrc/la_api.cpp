@@ -427,6 +427,16 @@ LA_API la_status layer_adam_step_device_step(const la_layer_desc* layer,
   return update(layer, hp, 0, 0, true, overflow_flag, nullptr, step_on_device, hip_stream);
 }
 
+LA_API la_status layer_adam_step_ex(const la_layer_desc* layer, const la_adam_params* hp,
+                                    const la_step_options* opts, void* hip_stream) {
+  const la_step_options defaults = {};
+  const la_step_options& o = opts != nullptr ? *opts : defaults;
+  if (o.use_range != 0 && o.use_range != 1)
+    return fail(LA_ERR_INVALID_ARGUMENT, "use_range = %d, need 0 or 1", o.use_range);
+  return update(layer, hp, o.elem_begin, o.elem_end, o.use_range == 0, o.overflow_flag,
+                o.skip_if_nonzero, o.step_on_device, hip_stream);
+}
+
 LA_API la_status la_check_gradients(const la_layer_desc* layer, double grad_unscale,
                                     int32_t* found_nonfinite, void* hip_stream) {
   la_status st = check_counts(layer);
@@ -517,6 +527,6 @@ LA_API int64_t la_traffic_bytes(const la_layer_desc* layer) {
 
 LA_API const char* la_last_error(void) { return g_error; }
 
-LA_API const char* la_version(void) { return "layeradam 0.5.0 gfx950"; }
+LA_API const char* la_version(void) { return "layeradam 0.6.0 gfx950"; }
 
 }  // extern "C"

@@ -116,6 +116,24 @@ int main(void) {
     fprintf(stderr, "layer_adam_step: %d %s\n", st, la_last_error());
     return 2;
   }
+  /* the combined entry point from C: an empty range enqueues nothing, an
+     unknown use_range is refused */
+  la_step_options opt;
+  memset(&opt, 0, sizeof opt);
+  opt.use_range = 1;
+  opt.elem_begin = opt.elem_end = 7;
+  opt.overflow_flag = flag;
+  st = layer_adam_step_ex(&layer, &hyper, &opt, stream);
+  if (st != LA_OK) {
+    fprintf(stderr, "layer_adam_step_ex: %d %s\n", st, la_last_error());
+    return 2;
+  }
+  opt.use_range = 2;
+  if (layer_adam_step_ex(&layer, &hyper, &opt, stream) != LA_ERR_INVALID_ARGUMENT ||
+      strlen(la_last_error()) == 0) {
+    fprintf(stderr, "use_range = 2 was not refused\n");
+    return 2;
+  }
   /* a refused call enqueues nothing and says why */
   la_adam_params bad = hyper;
   bad.step = 0;

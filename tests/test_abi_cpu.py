@@ -460,3 +460,67 @@ def test_direction_probe_of_an_empty_range_enqueues_nothing(part):
     desc, keep = la.make_layer([fake_tensor(0)], 2, la.GRAD_BF16)
     la.direction_probe_raw(desc, part, 40, 40)
     assert la.last_error() == ""
+
+
+@host_only
+@pytest.mark.parametrize("case", ["use_range_2", "range_past_end", "range_reversed",
+                                  "skip_misaligned", "skip_on_master", "step_misaligned",
+                                  "step_on_copy", "flag_misaligned", "bad_beta2_with_step",
+                                  "no_hyperparameters"])
+def test_step_ex_refusals(case):
+    """layer_adam_step_ex checks each option as its own entry point does, plus
+    use_range; nothing is enqueued on a refusal."""
+    t = fake_tensor(0)
+    desc, keep = la.make_layer([t], 2, la.GRAD_BF16)
+    hp = la.make_params(**HP)
+    opts = la.StepOptions(0, 0, 0, None, None, None)
+    if case == "use_range_2":
+        opts.use_range = 2
+    elif case == "range_past_end":
+        opts.use_range, opts.elem_begin, opts.elem_end = 1, 0, t["numel"] + 1
+    elif case == "range_reversed":
+        opts.use_range, opts.elem_begin, opts.elem_end = 1, 9, 8
+    elif case == "skip_misaligned":
+        opts.skip_if_nonzero = BASE + 0x50000002
+    elif case == "skip_on_master":
+        opts.skip_if_nonzero = t["master"] + 64
+    elif case == "step_misaligned":
+        opts.step_on_device = BASE + 0x50000004
+    elif case == "step_on_copy":
+        opts.step_on_device = t["weight_out"] + 16
+    elif case == "flag_misaligned":
+        opts.overflow_flag = BASE + 0x50000001
+    elif case == "bad_beta2_with_step":
+        opts.step_on_device = BASE + 0x50000000
+        hp = la.make_params(**dict(HP, beta2=1.0))
+    lib = la.load()
+    rc = lib.layer_adam_step_ex(ctypes.byref(desc),
+                                None if case == "no_hyperparameters" else ctypes.byref(hp),
+                                ctypes.byref(opts), None)
+    want = {"skip_misaligned": 2, "step_misaligned": 2, "flag_misaligned": 2,
+            "skip_on_master": 3, "step_on_copy": 3}.get(case, 1)
+    assert rc == want, (case, rc, la.last_error())
+    assert la.last_error()
+
+
+@host_only
+def test_step_ex_defaults_and_empty_range_enqueue_nothing_when_refused_or_empty():
+    """NULL options mean layer_adam_step (here refused for t = 0, the same
+    message as layer_adam_step); an empty element range launches nothing."""
+    desc, keep = la.make_layer([fake_tensor(0)], 2, la.GRAD_BF16)
+    lib = la.load()
+    bad = la.make_params(**dict(HP, step=0))
+    assert lib.layer_adam_step_ex(ctypes.byref(desc), ctypes.byref(bad), None, None) == 1
+    msg = la.last_error()
+    assert lib.layer_adam_step(ctypes.byref(desc), ctypes.byref(bad), None, None) == 1
+    assert la.last_error() == msg
+    la.step_ex_raw(desc, la.make_params(**HP), 100, 100)
+    assert la.last_error() == ""
+
+
+def test_binding_step_ex_needs_both_range_ends_and_a_step():
+    desc, keep = la.make_layer([dict(numel=0)], 2, la.GRAD_BF16)
+    with pytest.raises(ValueError):
+        la.step_ex_raw(desc, la.make_params(**HP), 0, None)
+    with pytest.raises(ValueError):
+        la._ex_params(1e-5, 0.9, 0.999, 1e-8, 0.0, None, 1.0, None)

@@ -88,6 +88,12 @@ many[200]["exp_avg"] = many[17]["weight_out"] + 64 if many[17]["numel"] > 64 els
 d, k = la.make_layer(many, 2, 0)
 refused(lib.layer_adam_step(ctypes.byref(d), ctypes.byref(hp), None, None))
 assert lib.la_state_bytes(ctypes.byref(d)) > 0 and lib.la_traffic_bytes(ctypes.byref(d)) > 0
+# the combined entry point: bad use_range, range, misaligned skip and step
+for o in (la.StepOptions(2, 0, 0, None, None, None), la.StepOptions(1, 5, 1 << 40, None, None, None),
+          la.StepOptions(0, 0, 0, None, BASE + 0x50000002, None),
+          la.StepOptions(0, 0, 0, None, None, BASE + 0x50000004)):
+    refused(lib.layer_adam_step_ex(ctypes.byref(d), ctypes.byref(hp), ctypes.byref(o), None))
+refused(lib.layer_adam_step_ex(ctypes.byref(d), ctypes.byref(bad_hp), None, None))
 # the direction probe: bad part, residency and range
 for part, lo, hi, wg in ((2, 0, 1024, -1), (0, 0, 1024, 65), (1, 0, 1024, -2), (0, 9, 3, -1),
                          (1, 0, 1 << 40, -1)):
