@@ -14,7 +14,10 @@ Prints one JSON line:
                ((2R + 26) * N) over the mean launch time from HIP events on
                the launch stream, against 8 TB/s; traffic = HBM bytes per
                launch from the committed rocprofv3 counter summary (null if
-               the kernel source changed since it was taken)
+               the kernel source changed since it was taken); the update's
+               rate also against the stream probe, the reference copy, and
+               (with the extras) its own loads and stores issued at once by
+               two kernels or one after the other
   stream_probe the library's stream probe on the same layer: the update's
                loads, stores and launch shape without its arithmetic -- the
                rate HBM gives this mix of R + 3 read and 4 write streams
@@ -763,7 +766,15 @@ def main():
         out["extras"]["producer_overlap"] = producer_overlap(torch, la, w, L, params, grads,
                                                              _flat, t + 1000)
         log("bench: direction split")
-        out["extras"]["direction_split"] = direction_split(torch, la, layer, w, mean_ms)
+        ds = direction_split(torch, la, layer, w, mean_ms)
+        out["extras"]["direction_split"] = ds
+        # the update against its own loads and stores issued at once by two
+        # kernels (the rate HBM gives reads and writes interleaved) and
+        # against the two run one after the other (what separating them in
+        # time would give)
+        out["roofline"]["mixed_ceiling_gbs"] = ds["at_once_two_streams"]["gbs"]
+        out["roofline"]["frac_of_mixed_ceiling"] = achieved / ds["at_once_two_streams"]["gbs"]
+        out["roofline"]["frac_of_in_sequence"] = achieved / ds["in_sequence"]["gbs"]
     del layer, params, grads, _flat
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
