@@ -769,11 +769,11 @@ def main():
         ds = direction_split(torch, la, layer, w, mean_ms)
         out["extras"]["direction_split"] = ds
         # the update against its own loads and stores issued at once by two
-        # kernels (the rate HBM gives reads and writes interleaved) and
-        # against the two run one after the other (what separating them in
-        # time would give)
-        out["roofline"]["mixed_ceiling_gbs"] = ds["at_once_two_streams"]["gbs"]
-        out["roofline"]["frac_of_mixed_ceiling"] = achieved / ds["at_once_two_streams"]["gbs"]
+        # kernels (how HBM serves the two directions interleaved) and against
+        # the two run one after the other (what separating them in time
+        # would give)
+        out["roofline"]["mixed_reference_gbs"] = ds["at_once_two_streams"]["gbs"]
+        out["roofline"]["frac_of_mixed_reference"] = achieved / ds["at_once_two_streams"]["gbs"]
         out["roofline"]["frac_of_in_sequence"] = achieved / ds["in_sequence"]["gbs"]
     del layer, params, grads, _flat
     torch.cuda.synchronize()
