@@ -537,14 +537,16 @@ def extras(torch, la, w, params, grads, t0):
                                  "overhead": ms / ms_whole - 1.0,
                                  "gbs": w.traffic_bytes / ms / 1e6}
     found = torch.zeros(1, dtype=torch.int32, device="cuda:0")
-    ms = time_launches(torch, lambda: la.check_gradients(grads, found, grad_unscale=w.unscale))
+    layer = la.Layer(params, grads)
+    ms = time_launches(torch, lambda: layer.check_gradients(found, grad_unscale=w.unscale),
+                       warm_ms=WARM_MS)
     out["check_gradients"] = {"ms": ms, "bytes_per_param": 2 * w.replicas,
                               "gbs": 2 * w.replicas * n / ms / 1e6}
 
     def gated():
         found.zero_()
-        la.check_gradients(grads, found, grad_unscale=w.unscale)
-        la.step_gated(params, grads, found, **hp())
+        layer.check_gradients(found, grad_unscale=w.unscale)
+        layer.step_gated(found, **hp())
 
     ms = time_launches(torch, gated)
     out["check_then_gated_step"] = {"ms": ms, "bytes_per_param": 4 * w.replicas + 26,
@@ -568,7 +570,6 @@ def extras(torch, la, w, params, grads, t0):
         torch.cuda.synchronize()
         return host
 
-    layer = la.Layer(params, grads)
     out["host_us_per_call"] = {
         "functional": host_us(lambda: la.step(params, grads, **hp())),
         "layer_object": host_us(lambda: layer.step(**hp())),
