@@ -83,8 +83,22 @@ int workgroups_per_cu_override() {
   return value;
 }
 
-// One workgroup per chunk up to this many; the kernel strides past it.
+// One workgroup per chunk up to this many; the kernels stride past it.
 constexpr int kMaxGrid = 1 << 30;
+
+// Most workgroups of one launch: kMaxGrid, or LAYERADAM_MAX_GRID (1..kMaxGrid,
+// read once), which lets a test drive the kernels' striding loops with
+// layers of ordinary size.
+int max_grid() {
+  static const int value = [] {
+    const char* env = std::getenv("LAYERADAM_MAX_GRID");
+    if (env == nullptr || *env == '\0') return kMaxGrid;
+    char* end = nullptr;
+    const long v = std::strtol(env, &end, 10);
+    return (*end == '\0' && v >= 1 && v <= kMaxGrid) ? static_cast<int>(v) : kMaxGrid;
+  }();
+  return value;
+}
 
 bool finite_nonneg(double x) { return std::isfinite(x) && x >= 0.0; }
 
@@ -293,7 +307,7 @@ la_status enqueue(const la_layer_desc* layer, Mode mode, const la::Scalars& s,
       hipError_t e = hipGetDevice(&device);
       if (e != hipSuccess)
         return fail(LA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
-      shape.grid_cap = kMaxGrid;
+      shape.grid_cap = max_grid();
       device_facts(device, &shape.lds_per_cu, &shape.lds_per_block);
       shape.wg_per_cu = wg_per_cu >= 0 ? wg_per_cu : workgroups_per_cu_override();
     }
@@ -506,7 +520,8 @@ LA_API la_status la_copy_reference(void* dst, const void* src, int64_t bytes,
   int lds_per_cu = 0, lds_per_block = 0;
   device_facts(device, &lds_per_cu, &lds_per_block);
   e = la::launch_copy_reference(dst, src, bytes / 16, lds_per_cu, lds_per_block,
-                                workgroups_per_cu_override(), static_cast<hipStream_t>(hip_stream));
+                                workgroups_per_cu_override(), max_grid(),
+                                static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess)
     return fail(LA_ERR_HIP, "copy launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -13,9 +13,11 @@ namespace la {
 // Enqueue dst[i] = src[i] for the n16 16-byte units of two disjoint, 16-byte
 // aligned buffers, on `stream`. lds_per_cu / lds_per_block: the device's LDS
 // sizes (0: unknown); wg_per_cu: resident workgroups per compute unit to aim
-// for (-1: the kernel's default, 0: no cap).
+// for (-1: the kernel's default, 0: no cap); grid_cap: most workgroups of the
+// launch (the kernel strides past it).
 hipError_t launch_copy_reference(void* dst, const void* src, int64_t n16, int lds_per_cu,
-                                 int lds_per_block, int wg_per_cu, hipStream_t stream);
+                                 int lds_per_block, int wg_per_cu, int grid_cap,
+                                 hipStream_t stream);
 
 // Parts of the direction probe.
 constexpr int kProbeReads = 0;   // read the R gradients and master, m, v; write nothing

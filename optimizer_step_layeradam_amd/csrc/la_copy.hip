@@ -263,10 +263,12 @@ hipError_t launch_direction_typed(const TensorArgs* ts, int count, int out_dtype
 }  // namespace
 
 hipError_t launch_copy_reference(void* dst, const void* src, int64_t n16, int lds_per_cu,
-                                 int lds_per_block, int wg_per_cu, hipStream_t stream) {
+                                 int lds_per_block, int wg_per_cu, int grid_cap,
+                                 hipStream_t stream) {
   if (n16 <= 0) return hipSuccess;
   const int64_t chunks = (n16 + kCopyChunk - 1) / kCopyChunk;
-  const int64_t grid = chunks < kCopyMaxGrid ? chunks : kCopyMaxGrid;
+  const int64_t cap = grid_cap >= 1 && grid_cap < kCopyMaxGrid ? grid_cap : kCopyMaxGrid;
+  const int64_t grid = chunks < cap ? chunks : cap;
   const int per_cu = wg_per_cu < 0 ? LA_COPY_WORKGROUPS_PER_CU : wg_per_cu;
   const int lds = reserved_lds(per_cu, lds_per_cu, lds_per_block);
   u32x4* d = static_cast<u32x4*>(dst);
