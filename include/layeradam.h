@@ -52,6 +52,12 @@
  * Thread safety: calls may come from several host threads at once. The only
  * global state is a thread-local error message and, per device, the LDS
  * sizes the launch shape is derived from (read once, atomically).
+ *
+ * Environment (each read once per process; for measurement and testing, the
+ * results do not depend on them): LAYERADAM_WORKGROUPS_PER_CU (0..64)
+ * replaces every kernel's resident-workgroups-per-compute-unit default, 0
+ * meaning no cap; LAYERADAM_MAX_GRID (1..2^30) lowers the most workgroups
+ * one launch may have, past which the kernels stride.
  */
 #ifndef LAYERADAM_H
 #define LAYERADAM_H
