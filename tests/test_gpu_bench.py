@@ -69,3 +69,35 @@ def test_bench_prints_one_consistent_json_line():
     assert cb["unit"] == "Gparam/s" and cb["sample"]
     par = cb["parity_vs_gpu_first_step"]
     assert par["params"] > 0 and par["max_ulp"] <= 2 and par["bf16_mismatch"] == 0
+
+
+def test_bench_extras_on_a_smaller_layer():
+    """The extras (everything after the timed region) on the Qwen3-4B-shaped
+    layer: present, and consistent with the byte model."""
+    print("case bench.py --workload qwen3_4b_layer (extras)", flush=True)
+    r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--workload",
+                        "qwen3_4b_layer", "--steps", "3", "--warmup", "1", "--no-per-workload",
+                        "--cpu-seconds", "1"], capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads([x for x in r.stdout.splitlines() if x.strip()][-1])
+    w = synth.WORKLOADS["qwen3_4b_layer"]
+    x = d["extras"]
+    for k in ("range_64MiB_chunks", "check_gradients", "check_then_gated_step",
+              "fp16_compute_copy", "no_compute_copy", "host_us_per_call", "one_shard_of_g",
+              "host_resident_state", "producer_overlap", "direction_split"):
+        assert k in x, k
+    ds = x["direction_split"]
+    assert ds["read_bytes_per_param"] == 2 * w.replicas + 12
+    assert ds["read_bytes_per_param"] + ds["write_bytes_per_param"] == w.bytes_per_param
+    for k in ("reads_alone", "writes_alone", "at_once_two_streams"):
+        assert ds[k]["ms"] > 0 and 0.0 < ds[k]["frac"] < 1.0, k
+    assert ds["in_sequence"]["ms"] == pytest.approx(ds["reads_alone"]["ms"] +
+                                                    ds["writes_alone"]["ms"], rel=1e-9)
+    assert set(ds["alternating_phases"]) == {"1", "4", "16", "64"}
+    rf = d["roofline"]
+    assert rf["frac_of_mixed_reference"] == pytest.approx(
+        rf["achieved"] / ds["at_once_two_streams"]["gbs"], rel=1e-9)
+    for p in ("gemm", "host_link"):
+        e = x["producer_overlap"][p]
+        assert e["gradients_reproduced"] is True
+        assert e["overlapped_ms"] > 0 and e["producer_ms"] > 0 and e["update_ms"] > 0
