@@ -311,10 +311,10 @@ LA_API int64_t la_state_bytes(const la_layer_desc *layer);
  * + the 2-byte compute copy ((2R + 24) with LA_OUT_NONE). This is the W of
  * the one resource the update uses in the step-time bound T >= max_j W_j /
  * beta_j of "SlideDP: Scaling Host-Resident LLM Fine-Tuning Across Multiple
- * GPUs" (研究动机, and 技术新颖性 for the per-resource minimum duration
- * W_j / beta_j): with HBM the only resource, a launch takes at least these
- * bytes over the HBM bandwidth. -1 if the descriptor is invalid. Host
- * only. */
+ * GPUs" (stated in 研究动机; 核心方法 builds its analytic step-time model on
+ * it; 技术新颖性 gives the per-resource minimum duration W_j / beta_j): with
+ * HBM the only resource, a launch takes at least these bytes over the HBM
+ * bandwidth. -1 if the descriptor is invalid. Host only. */
 LA_API int64_t la_traffic_bytes(const la_layer_desc *layer);
 
 /* Message of the calling thread's last failed call ("" if none). The pointer
