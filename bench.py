@@ -27,9 +27,11 @@ Prints one JSON line:
   extras       the neighbouring entry points on the same layer (chunked
                range updates, finite check and gated step, other copy
                formats, one GPU's shard, host-resident state), the
-               per-chunk overlap of the update with two gradient producers,
-               and the update's traffic split by direction (its loads alone,
-               its stores alone, in sequence, at once, alternating by slice)
+               the update and the stream probe with 1, 2, 4 and all R
+               replicas, the per-chunk overlap of the update with two
+               gradient producers, and the update's traffic split by
+               direction (its loads alone, its stores alone, in sequence, at
+               once, alternating by slice)
   cpu_baseline the CPU oracle timed on this host (one core) on a bounded
                prefix of the same layer, with its parity against the GPU's
                first step on that prefix
@@ -453,6 +455,31 @@ def producer_overlap(torch, la, w, L, params, grads, flat, t0, k=1024, reps=3,
     return out
 
 
+def replica_sweep(torch, la, w, params, grads, t0, reps=10):
+    """The update and its stream probe on the resident layer with the first R
+    of its gradient replicas, R = 1, 2, 4 and the layer's own: (2R + 26)
+    B/param, so fewer read streams and a smaller read share."""
+    out = {}
+    t = [t0]
+    for R in sorted({1, 2, 4, w.replicas}):
+        if R > w.replicas:
+            continue
+        layer = la.Layer(params, [g[:R] for g in grads])
+        nbytes = (2 * R + 26) * w.numel
+
+        def one():
+            layer.step(step=t[0], grad_unscale=w.unscale, **w.hyper)
+            t[0] += 1
+
+        entry = {}
+        for k, fn in (("update", one), ("probe", layer.stream_probe)):
+            ms = time_launches(torch, fn, reps=reps, warm=3, warm_ms=WARM_MS)
+            entry[k] = {"ms": ms, "gbs": nbytes / ms / 1e6, "frac": nbytes / ms / 1e6 / PEAK_HBM_GBS}
+        entry["bytes_per_param"] = 2 * R + 26
+        out[str(R)] = entry
+    return out
+
+
 def direction_split(torch, la, layer, w, update_ms, reps=10):
     """The update's traffic taken apart by direction on the resident layer,
     with the library's direction probe: its loads alone ((2R + 12) B/param),
@@ -763,6 +790,7 @@ def main():
     out["roofline"]["frac_of_copy_reference"] = achieved / out["hbm_copy_reference"]["gbs"]
     if not args.no_extras:
         out["extras"] = extras(torch, la, w, params, grads, t)
+        out["extras"]["replica_sweep"] = replica_sweep(torch, la, w, params, grads, t + 500)
         log("bench: producer overlap")
         out["extras"]["producer_overlap"] = producer_overlap(torch, la, w, L, params, grads,
                                                              _flat, t + 1000)

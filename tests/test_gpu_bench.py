@@ -84,8 +84,14 @@ def test_bench_extras_on_a_smaller_layer():
     x = d["extras"]
     for k in ("range_64MiB_chunks", "check_gradients", "check_then_gated_step",
               "fp16_compute_copy", "no_compute_copy", "host_us_per_call", "one_shard_of_g",
-              "host_resident_state", "producer_overlap", "direction_split"):
+              "host_resident_state", "producer_overlap", "direction_split", "replica_sweep"):
         assert k in x, k
+    assert set(x["replica_sweep"]) == {"1", "2", "4"}   # the 4B layer has R = 4
+    for R, e in x["replica_sweep"].items():
+        assert e["bytes_per_param"] == 2 * int(R) + 26
+        for k in ("update", "probe"):
+            assert e[k]["gbs"] == pytest.approx(e["bytes_per_param"] * w.numel / e[k]["ms"] / 1e6,
+                                                rel=1e-9)
     ds = x["direction_split"]
     assert ds["read_bytes_per_param"] == 2 * w.replicas + 12
     assert ds["read_bytes_per_param"] + ds["write_bytes_per_param"] == w.bytes_per_param
