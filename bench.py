@@ -36,7 +36,7 @@ Prints one JSON line:
                prefix of the same layer, with its parity against the GPU's
                first step on that prefix
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME | --config NAME]
 """
 from __future__ import annotations
 
@@ -650,7 +650,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default=None)
+    ap.add_argument("--workload", "--config", dest="workload", default=None,
+                    help="workload to time (default qwen3_14b_layer): " + ", ".join(
+                        ("tiny", "qwen3_4b_layer", "qwen3_14b_layer", "flat_800m",
+                         "qwen25_72b_layer")))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
